@@ -1,0 +1,275 @@
+"""Benchmark: 2-bit decode-attention step over a KIVI-style low-bit KV cache, 1 GPU.
+
+A step is one pass of the whole hot path: append one token per sequence (FP16
+window write, and a group quantize + pack whenever a group leaves the window),
+then decode attention over every cached token (split kernel + combine kernel).
+
+Workload (default): GQA layer, batch 1, 32 query / 8 KV heads, head_dim 128,
+context 131072, 2-bit, G = 32, R = 128. Several independent caches are built and
+stepped round-robin so that consecutive steps never find their cache in the
+256 MB last-level cache: the reported bandwidth is HBM bandwidth.
+
+Prints one JSON line. `value` is the effective bandwidth of a whole step:
+algorithmic bytes (packed codes + fp16 scales/zero-points + fp16 window) divided
+by the step time. `roofline` reports the dominant kernel (the decode split
+kernel) timed with HIP events recorded around it on its own stream.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import kvq_workloads as wl  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through the HIP runtime (timed on any stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p(0)
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float(0)
+        if self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def gpu_kv(torch, w, mult, off, B, n, gen, dev):
+    """Seeded fp16 keys/values [B, n, Hkv, D] with the workload's distribution."""
+    shape = (B, n, w.num_kv_heads, w.head_dim)
+    k = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    k = (mult * (k + off)).to(torch.float16)
+    v = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.float16)
+    return k.contiguous(), v.contiguous()
+
+
+def build_caches(torch, kvq, w, copies, max_tokens, dev, gps):
+    mult = torch.tensor(np.stack([wl.key_channel_params(w, h)[0] for h in range(w.num_kv_heads)]), device=dev)
+    off = torch.tensor(np.stack([wl.key_channel_params(w, h)[1] for h in range(w.num_kv_heads)]), device=dev)
+    caches = []
+    lens = w.context_lengths()
+    chunk = 16384
+    for c in range(copies):
+        cache = kvq.KVCache(w.batch, w.num_q_heads, w.num_kv_heads, bits=w.bits, group=w.group,
+                            residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=dev)
+        if gps:
+            cache.set_decode_split(gps)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed * 1000 + c)
+        done = np.zeros(w.batch, dtype=np.int64)
+        while np.any(done < lens):
+            n = np.minimum(lens - done, chunk)
+            k, v = gpu_kv(torch, w, mult, off, w.batch, int(n.max()), gen, dev)
+            cache.append(k, v, n.tolist())
+            done += n
+        caches.append(cache)
+    torch.cuda.synchronize()
+    return caches, mult, off
+
+
+def step_bytes(cache, w):
+    total = 0
+    for b in range(w.batch):
+        T, Q = cache.seq_len(b)
+        total += w.num_kv_heads * wl.algorithmic_bytes(T, Q, w.bits, w.group, w.head_dim)
+    return total
+
+
+def cpu_baseline(w, heads=4, steps=3):
+    """Time the CPU oracle (single BLAS thread) on `heads` KV heads of sequence 0 at
+    the workload's full context: per step, append one token and attend."""
+    from threadpoolctl import threadpool_limits
+    from oracle import OracleHead
+    ratio = w.num_q_heads // w.num_kv_heads
+    T0 = int(w.context_lengths()[0])
+    with threadpool_limits(1):
+        hs = []
+        for h in range(heads):
+            oh = OracleHead(w.bits, w.residual, w.rotate)
+            oh.append(wl.keys(w, 0, h, 0, T0), wl.values(w, 0, h, 0, T0))
+            hs.append(oh)
+        nbytes = 0
+        t0 = time.perf_counter()
+        for s in range(steps):
+            q = wl.queries(w, s)[0]
+            for h, oh in enumerate(hs):
+                oh.append(wl.keys(w, 0, h, oh.T, oh.T + 1), wl.values(w, 0, h, oh.T, oh.T + 1))
+                oh.attend(q[h * ratio:(h + 1) * ratio])
+                nbytes += wl.algorithmic_bytes(oh.T, oh.Q, w.bits, w.group, w.head_dim)
+        dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequence 0, kv-heads 0..{heads - 1} (each with its {ratio} query heads) of "
+                      f"{w.name} at full context {T0}, {steps} steps of append-1 + attend; "
+                      f"{dt:.1f} s timed, numpy with one BLAS thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa_128k_2bit", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--copies", type=int, default=8, help="independent caches stepped round-robin")
+    ap.add_argument("--groups-per-split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters, if present")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels are per-GPU and "
+              f"this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_asymmetric_kv_amd as kvq
+    kvq.load()
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[args.workload]
+    total_steps = args.warmup + args.steps
+    max_tokens = int(w.context_lengths().max()) + total_steps + 1
+    print(f"[bench] building {args.copies} caches of {w.name}", file=sys.stderr, flush=True)
+    caches, mult, off = build_caches(torch, kvq, w, args.copies, max_tokens, dev, args.groups_per_split)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed * 7919)
+    knew, vnew = gpu_kv(torch, w, mult, off, total_steps * w.batch, 1, gen, dev)
+    knew = knew.view(total_steps, w.batch, 1, w.num_kv_heads, w.head_dim)
+    vnew = vnew.view(total_steps, w.batch, 1, w.num_kv_heads, w.head_dim)
+    q = torch.randn((total_steps, w.batch, w.num_q_heads, w.head_dim), generator=gen, device=dev).to(torch.float16)
+    outs = [torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev) for _ in caches]
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = ev.create(total_steps)
+    en = ev.create(total_steps)
+    ks = ev.create(total_steps)
+    ke = ev.create(total_steps)
+    nbytes = []
+    print(f"[bench] {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    host_t0 = None
+    for s in range(total_steps):
+        if s == args.warmup:
+            host_t0 = time.perf_counter()
+        c = caches[s % len(caches)]
+        ev.record(st[s], stream)
+        c.append(knew[s].contiguous(), vnew[s].contiguous())
+        c.set_profile_events(ks[s], ke[s])
+        c.decode(q[s].contiguous(), outs[s % len(caches)])
+        ev.record(en[s], stream)
+        nbytes.append(step_bytes(c, w))
+    host_enqueue_s = time.perf_counter() - host_t0
+    torch.cuda.synchronize()
+    for c in caches:
+        c.set_profile_events(0, 0)
+    timed = range(args.warmup, total_steps)
+    total_ms = ev.elapsed_ms(st[args.warmup], en[total_steps - 1])
+    step_ms = [ev.elapsed_ms(st[s], en[s]) for s in timed]
+    kern_ms = [ev.elapsed_ms(ks[s], ke[s]) for s in timed]
+    bytes_avg = float(np.mean([nbytes[s] for s in timed]))
+    ms_per_step = total_ms / args.steps
+    kern_avg_ms = float(np.mean(kern_ms))
+    achieved = bytes_avg / (kern_avg_ms * 1e-3) / 1e9
+    value = bytes_avg / (ms_per_step * 1e-3) / 1e9
+    out_ok = all(bool(torch.isfinite(o).all()) for o in outs)
+
+    # warm (last-level-cache resident) decode of one cache, for reference only
+    warm = []
+    c = caches[0]
+    qw = q[0].contiguous()
+    for i in range(30):
+        ev.record(st[i], stream)
+        c.decode(qw, outs[0])
+        ev.record(en[i], stream)
+    torch.cuda.synchronize()
+    warm = [ev.elapsed_ms(st[i], en[i]) for i in range(10, 30)]
+    for e in (st, en, ks, ke):
+        ev.destroy(e)
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                t = json.load(f)
+            if t.get("workload") == w.name:
+                traffic = t.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
+
+    result = {
+        "metric": "2-bit decode-attention µs/step + effective HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "context": int(w.context_lengths().max()), "bits": w.bits,
+                   "group": w.group, "residual": w.residual, "rotate": w.rotate,
+                   "caches_round_robin": len(caches), "parallelism": "single GPU"},
+        "step": {"algorithmic_bytes": int(bytes_avg), "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+                 "p10_us": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
+                 "p50_us": round(float(np.percentile(step_ms, 50)) * 1e3, 2),
+                 "p90_us": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+                 "decode_split_kernel_us": round(kern_avg_ms * 1e3, 2),
+                 "warm_decode_attention_us": round(float(np.median(warm)) * 1e3, 2),
+                 "host_enqueue_us_per_step": round(host_enqueue_s / args.steps * 1e6, 2),
+                 "outputs_finite": out_ok},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": f"decode_split_kernel<{w.bits},{w.num_q_heads // w.num_kv_heads}>"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,7 @@
+"""MI355X-native decode attention over a KIVI-style asymmetric low-bit KV cache.
+
+The compute path is the HIP library libkvq.so (C ABI in include/kvq.h); this
+package only binds it.
+"""
+from ._lib import (KVCache, KVQConfig, KVQError, cache_bytes, group_bytes, load,  # noqa: F401
+                   make_config)

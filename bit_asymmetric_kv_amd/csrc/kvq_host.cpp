@@ -1,0 +1,346 @@
+// Host side of the C ABI: argument validation, memory layout, the host mirror of
+// per-sequence lengths, the residual-window bookkeeping, and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+using kvq::Layout;
+using kvq::SeqDesc;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvq_status fail(kvq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kvq_status ok() {
+  g_err[0] = '\0';
+  return KVQ_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Quantized-token count of the residual rule: G * floor(max(0, T - R) / G).
+int64_t quantized_count(int64_t T, int64_t R) {
+  int64_t over = T - R;
+  if (over <= 0) return 0;
+  return (over / kvq::kGroup) * kvq::kGroup;
+}
+
+kvq_status validate(const kvq_config* cfg) {
+  if (!cfg) return fail(KVQ_ERR_INVALID_ARG, "config is NULL");
+  if (cfg->batch < 1) return fail(KVQ_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", cfg->batch);
+  if (cfg->num_kv_heads < 1) return fail(KVQ_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (cfg->num_q_heads < 1 || cfg->num_q_heads % cfg->num_kv_heads)
+    return fail(KVQ_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                cfg->num_q_heads, cfg->num_kv_heads);
+  int ratio = cfg->num_q_heads / cfg->num_kv_heads;
+  if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 8)
+    return fail(KVQ_ERR_INVALID_ARG, "num_q_heads / num_kv_heads must be 1, 2, 4 or 8 (got %d)", ratio);
+  if (cfg->head_dim != kvq::kHeadDim)
+    return fail(KVQ_ERR_INVALID_ARG, "head_dim must be 128 (got %d)", cfg->head_dim);
+  if (cfg->bits != 2 && cfg->bits != 4)
+    return fail(KVQ_ERR_INVALID_ARG, "bits must be 2 or 4 (got %d)", cfg->bits);
+  if (cfg->group != kvq::kGroup)
+    return fail(KVQ_ERR_INVALID_ARG, "group must be 32 (got %d)", cfg->group);
+  if (cfg->head_dim % cfg->group)
+    return fail(KVQ_ERR_INVALID_ARG, "head_dim must be a multiple of group");
+  if (cfg->residual < 0 || cfg->residual % cfg->group || cfg->residual > 4096)
+    return fail(KVQ_ERR_INVALID_ARG, "residual must be a multiple of group in [0, 4096] (got %d)",
+                cfg->residual);
+  if (cfg->rotate != 0 && cfg->rotate != 1) return fail(KVQ_ERR_INVALID_ARG, "rotate must be 0 or 1");
+  if (cfg->max_tokens < 1 || cfg->max_tokens > (int64_t(1) << 30))
+    return fail(KVQ_ERR_INVALID_ARG, "max_tokens must be in [1, 2^30]");
+  if (!(cfg->softmax_scale >= 0.0f) || std::isinf(cfg->softmax_scale))
+    return fail(KVQ_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  return ok();
+}
+
+Layout make_layout(const kvq_config* cfg) {
+  Layout L{};
+  L.B = cfg->batch;
+  L.Hq = cfg->num_q_heads;
+  L.Hkv = cfg->num_kv_heads;
+  L.bits = cfg->bits;
+  L.R = cfg->residual;
+  L.W = cfg->residual + kvq::kGroup;
+  L.gcap = (cfg->max_tokens + kvq::kGroup - 1) / kvq::kGroup;
+  L.group_bytes = kvq_group_bytes(cfg->bits);
+  int64_t ms = (L.gcap + kvq::kMinGroupsPerSplit - 1) / kvq::kMinGroupsPerSplit;
+  L.max_splits = int32_t(std::max<int64_t>(1, std::min<int64_t>(ms, kvq::kMaxSplits)));
+  size_t off = 0;
+  L.seq_off = off;
+  off = align256(off + sizeof(SeqDesc) * size_t(L.B));
+  L.blocks_off = off;
+  off = align256(off + size_t(L.B) * L.Hkv * size_t(L.gcap) * L.group_bytes);
+  size_t ring = size_t(L.B) * L.Hkv * L.W * kvq::kHeadDim * 2;
+  L.ringk_off = off;
+  off = align256(off + ring);
+  L.ringv_off = off;
+  off = align256(off + ring);
+  L.part_off = off;
+  off = align256(off + size_t(L.B) * L.Hq * size_t(L.max_splits + 1) * kvq::kPartialStride * 4);
+  L.total = off;
+  return L;
+}
+
+constexpr int kStaging = 8;  // pinned upload buffers in flight per cache
+
+}  // namespace
+
+struct kvq_cache {
+  kvq_config cfg;
+  Layout L;
+  uint8_t* base = nullptr;
+  bool owned = false;
+  int device = 0;
+  hipStream_t create_stream = nullptr;
+  std::vector<int64_t> T, Q;
+  int32_t groups_per_split = 0;
+  hipEvent_t prof_start = nullptr, prof_stop = nullptr;
+  SeqDesc* staging[kStaging] = {};
+  hipEvent_t staging_done[kStaging] = {};
+  int next_staging = 0;
+};
+
+extern "C" {
+
+size_t kvq_group_bytes(int32_t bits) {
+  if (bits != 2 && bits != 4) return 0;
+  return size_t(2) * kvq::kGroup * kvq::kHeadDim * bits / 8 + 512 + 512;
+}
+
+const char* kvq_last_error(void) { return g_err; }
+
+kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes) {
+  kvq_status s = validate(cfg);
+  if (s != KVQ_OK) return s;
+  if (!bytes) return fail(KVQ_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = make_layout(cfg).total;
+  return ok();
+}
+
+void kvq_destroy(kvq_cache* c) {
+  if (!c) return;
+  hipSetDevice(c->device);
+  hipStreamSynchronize(c->create_stream);
+  for (int i = 0; i < kStaging; i++) {
+    if (c->staging_done[i]) {
+      hipEventSynchronize(c->staging_done[i]);
+      hipEventDestroy(c->staging_done[i]);
+    }
+    if (c->staging[i]) hipHostFree(c->staging[i]);
+  }
+  if (c->owned && c->base) hipFree(c->base);
+  delete c;
+}
+
+kvq_status kvq_create(const kvq_config* cfg, void* dev_mem, size_t dev_bytes, hipStream_t stream,
+                      kvq_cache** out) {
+  kvq_status s = validate(cfg);
+  if (s != KVQ_OK) return s;
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  Layout L = make_layout(cfg);
+  if (dev_mem && dev_bytes < L.total)
+    return fail(KVQ_ERR_OOM, "dev_bytes %zu < required %zu", dev_bytes, L.total);
+  if (dev_mem && (reinterpret_cast<uintptr_t>(dev_mem) & 255))
+    return fail(KVQ_ERR_INVALID_ARG, "dev_mem must be 256-byte aligned");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return fail(KVQ_ERR_NO_DEVICE, "no HIP device available");
+  }
+  kvq_cache* c = new (std::nothrow) kvq_cache();
+  if (!c) return fail(KVQ_ERR_OOM, "host allocation failed");
+  c->cfg = *cfg;
+  if (c->cfg.softmax_scale == 0.0f) c->cfg.softmax_scale = 1.0f / std::sqrt(float(cfg->head_dim));
+  c->L = L;
+  c->create_stream = stream;
+  c->T.assign(cfg->batch, 0);
+  c->Q.assign(cfg->batch, 0);
+  hipGetDevice(&c->device);
+  if (dev_mem) {
+    c->base = static_cast<uint8_t*>(dev_mem);
+  } else {
+    if (hipMalloc(reinterpret_cast<void**>(&c->base), L.total) != hipSuccess) {
+      (void)hipGetLastError();
+      delete c;
+      return fail(KVQ_ERR_OOM, "hipMalloc of %zu bytes failed", L.total);
+    }
+    c->owned = true;
+  }
+  for (int i = 0; i < kStaging; i++) {
+    if (hipHostMalloc(reinterpret_cast<void**>(&c->staging[i]), sizeof(SeqDesc) * cfg->batch) !=
+            hipSuccess ||
+        hipEventCreateWithFlags(&c->staging_done[i], hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      kvq_destroy(c);
+      return fail(KVQ_ERR_HIP, "pinned staging allocation failed");
+    }
+  }
+  if (hipMemsetAsync(c->base + L.seq_off, 0, sizeof(SeqDesc) * cfg->batch, stream) != hipSuccess) {
+    kvq_destroy(c);
+    return fail(KVQ_ERR_HIP, "clearing sequence state failed: %s", hipGetErrorString(hipGetLastError()));
+  }
+  *out = c;
+  return ok();
+}
+
+kvq_status kvq_seq_len(const kvq_cache* c, int32_t b, int64_t* T, int64_t* Q) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  if (b < 0 || b >= c->cfg.batch) return fail(KVQ_ERR_INVALID_ARG, "sequence index %d out of range", b);
+  if (T) *T = c->T[b];
+  if (Q) *Q = c->Q[b];
+  return ok();
+}
+
+kvq_status kvq_set_decode_split(kvq_cache* c, int32_t groups_per_split) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  if (groups_per_split != 0 &&
+      (groups_per_split < kvq::kMinGroupsPerSplit || groups_per_split > (1 << 20)))
+    return fail(KVQ_ERR_INVALID_ARG, "groups_per_split must be 0 or in [%d, 2^20]",
+                kvq::kMinGroupsPerSplit);
+  c->groups_per_split = groups_per_split;
+  return ok();
+}
+
+kvq_status kvq_set_profile_events(kvq_cache* c, hipEvent_t start, hipEvent_t stop) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(KVQ_ERR_INVALID_ARG, "start and stop must both be set or both be NULL");
+  c->prof_start = start;
+  c->prof_stop = stop;
+  return ok();
+}
+
+kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, const int32_t* n_tokens,
+                      int32_t n_max, hipStream_t stream) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  const int B = c->cfg.batch;
+  if (n_max < 0) return fail(KVQ_ERR_INVALID_ARG, "n_max must be >= 0");
+  int64_t total_new = 0;
+  for (int b = 0; b < B; b++) {
+    int64_t n = n_tokens ? n_tokens[b] : n_max;
+    if (n < 0 || n > n_max)
+      return fail(KVQ_ERR_INVALID_ARG, "n_tokens[%d] = %lld outside [0, n_max=%d]", b, (long long)n, n_max);
+    if (c->T[b] + n > c->cfg.max_tokens)
+      return fail(KVQ_ERR_CAPACITY, "sequence %d would hold %lld tokens > max_tokens %lld", b,
+                  (long long)(c->T[b] + n), (long long)c->cfg.max_tokens);
+    total_new += n;
+  }
+  if (total_new == 0) return ok();
+  if (!k || !v) return fail(KVQ_ERR_INVALID_ARG, "k and v must be device pointers when tokens are appended");
+
+  // Host bookkeeping: new lengths, groups leaving the window, tokens entering it.
+  int slot = c->next_staging;
+  c->next_staging = (slot + 1) % kStaging;
+  if (hipEventSynchronize(c->staging_done[slot]) != hipSuccess)
+    return fail(KVQ_ERR_HIP, "waiting for a staging buffer failed: %s", hipGetErrorString(hipGetLastError()));
+  SeqDesc* d = c->staging[slot];
+  int32_t max_flush = 0, max_ring = 0;
+  std::vector<int64_t> T2(B), Q2(B);
+  for (int b = 0; b < B; b++) {
+    int64_t n = n_tokens ? n_tokens[b] : n_max;
+    T2[b] = c->T[b] + n;
+    Q2[b] = quantized_count(T2[b], c->cfg.residual);
+    d[b].t_old = int32_t(c->T[b]);
+    d[b].n_new = int32_t(n);
+    d[b].q_old = int32_t(c->Q[b]);
+    d[b].q_new = int32_t(Q2[b]);
+    max_flush = std::max<int32_t>(max_flush, int32_t((Q2[b] - c->Q[b]) / kvq::kGroup));
+    // appended tokens that stay in the FP16 window
+    int64_t first_kept = std::max<int64_t>(c->T[b], Q2[b]);
+    max_ring = std::max<int32_t>(max_ring, int32_t(std::max<int64_t>(0, T2[b] - first_kept)));
+  }
+  SeqDesc* dev_seq = reinterpret_cast<SeqDesc*>(c->base + c->L.seq_off);
+  if (hipMemcpyAsync(dev_seq, d, sizeof(SeqDesc) * B, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipEventRecord(c->staging_done[slot], stream) != hipSuccess)
+    return fail(KVQ_ERR_HIP, "uploading sequence state failed: %s", hipGetErrorString(hipGetLastError()));
+  hipError_t e = hipSuccess;
+  if (max_flush > 0)
+    e = kvq::launch_flush(c->L, c->base, dev_seq, k, v, n_max, max_flush, c->cfg.rotate, stream);
+  if (e == hipSuccess && max_ring > 0)
+    e = kvq::launch_ring_write(c->L, c->base, dev_seq, k, v, n_max, max_ring, c->cfg.rotate, stream);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append kernels failed: %s", hipGetErrorString(e));
+  c->T = T2;
+  c->Q = Q2;
+  return ok();
+}
+
+kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, hipStream_t stream) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q and out must be device pointers");
+  int64_t max_groups = 0;
+  for (int b = 0; b < c->cfg.batch; b++) {
+    if (c->T[b] == 0) return fail(KVQ_ERR_EMPTY, "sequence %d holds no token", b);
+    max_groups = std::max(max_groups, c->Q[b] / kvq::kGroup);
+  }
+  int64_t gps = c->groups_per_split;
+  if (gps == 0) {
+    // Aim for about 2048 workgroups over the whole batch (8 per CU on 256 CUs)
+    // while giving each of the 4 waves of a workgroup a few groups to stream.
+    int64_t work = max_groups * c->cfg.batch * c->cfg.num_kv_heads;
+    gps = std::max<int64_t>(16, (work + 2047) / 2048);
+  }
+  int64_t nsplit = max_groups == 0 ? 0 : (max_groups + gps - 1) / gps;
+  if (nsplit > c->L.max_splits) {
+    gps = (max_groups + c->L.max_splits - 1) / c->L.max_splits;
+    nsplit = (max_groups + gps - 1) / gps;
+  }
+  const float scale_log2 = c->cfg.softmax_scale * 1.4426950408889634f;
+  const SeqDesc* dev_seq = reinterpret_cast<const SeqDesc*>(c->base + c->L.seq_off);
+  hipError_t e = kvq::launch_decode(c->L, c->base, dev_seq, q, out, int32_t(gps), int32_t(nsplit),
+                                    scale_log2, c->cfg.rotate, stream, c->prof_start, c->prof_stop);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode kernels failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kvq_status kvq_read_state(kvq_cache* c, int32_t part, int32_t b, int32_t h, size_t offset,
+                          void* host_dst, size_t bytes, hipStream_t stream) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  if (b < 0 || b >= c->cfg.batch || h < 0 || h >= c->cfg.num_kv_heads)
+    return fail(KVQ_ERR_INVALID_ARG, "(b, h) = (%d, %d) out of range", b, h);
+  if (!host_dst && bytes) return fail(KVQ_ERR_INVALID_ARG, "host_dst is NULL");
+  const Layout& L = c->L;
+  size_t region, start;
+  size_t bh = size_t(b) * L.Hkv + h;
+  switch (part) {
+    case KVQ_PART_GROUPS:
+      region = size_t(L.gcap) * L.group_bytes;
+      start = L.blocks_off + bh * region;
+      break;
+    case KVQ_PART_RING_K:
+    case KVQ_PART_RING_V:
+      region = size_t(L.W) * kvq::kHeadDim * 2;
+      start = (part == KVQ_PART_RING_K ? L.ringk_off : L.ringv_off) + bh * region;
+      break;
+    default:
+      return fail(KVQ_ERR_INVALID_ARG, "unknown part %d", part);
+  }
+  if (offset > region || bytes > region - offset)
+    return fail(KVQ_ERR_INVALID_ARG, "range [%zu, %zu) exceeds the part's %zu bytes", offset,
+                offset + bytes, region);
+  if (bytes == 0) return ok();
+  if (hipMemcpyAsync(host_dst, c->base + start + offset, bytes, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(KVQ_ERR_HIP, "reading state failed: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+}  // extern "C"

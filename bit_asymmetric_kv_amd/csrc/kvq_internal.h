@@ -1,0 +1,43 @@
+// Internal declarations shared by the host library and its kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;
+constexpr int kGroup = 32;
+constexpr int kPartialStride = kHeadDim + 2;  // m (log2 domain), l, o[128] per partial
+constexpr int kMinGroupsPerSplit = 4;
+constexpr int kMaxSplits = 2048;
+
+// Per-sequence record kept on the device and rewritten by every append:
+// tokens before the append, tokens appended, quantized tokens before and after.
+struct SeqDesc {
+  int32_t t_old;
+  int32_t n_new;
+  int32_t q_old;
+  int32_t q_new;
+};
+
+struct Layout {
+  int32_t B, Hq, Hkv, bits, R, W;  // W = R + G ring slots
+  int64_t gcap;                     // group blocks per (b, h)
+  size_t group_bytes;
+  int32_t max_splits;
+  size_t seq_off, blocks_off, ringk_off, ringv_off, part_off, total;
+};
+
+// Launchers (return hipGetLastError() of the launch).
+hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* k,
+                        const void* v, int32_t n_max, int32_t max_flush_groups, int rotate,
+                        hipStream_t stream);
+hipError_t launch_ring_write(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* k,
+                             const void* v, int32_t n_max, int32_t max_ring_tokens, int rotate,
+                             hipStream_t stream);
+hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* q,
+                         float* out, int32_t groups_per_split, int32_t nsplit, float scale_log2,
+                         int rotate, hipStream_t stream, hipEvent_t prof_start, hipEvent_t prof_stop);
+
+}  // namespace kvq

@@ -1,0 +1,161 @@
+/*
+ * kvq.h -- C ABI of a decode-attention library over a KIVI-style asymmetric
+ * low-bit KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The cache follows the pages' statement of the problem:
+ *  - keys are quantized per channel over groups of G tokens, values per token
+ *    over groups of G channels, each group with a min/max scale and zero-point
+ *    ("The Asymmetric Key-Value Cache Compression Framework", Summary and
+ *    Method; "KV cache quantization: putting the bits in the cached vectors",
+ *    full-text-skim notes on KIVI);
+ *  - codes use a fixed number of bits per element, 2 or 4 ("Read What Matters",
+ *    the NOVA-KV abstract on a fixed per-token bit count; "KVQuant" review,
+ *    Problem and Results on 2..4-bit widths);
+ *  - the most recent R tokens stay FP16 ("The Asymmetric Key-Value Cache
+ *    Compression Framework", In practice), and quantized groups are appended along
+ *    the token dimension and combined with that FP16 residual inside attention
+ *    ("KV cache quantization ...", full-text-skim notes on the grouped/residual
+ *    split);
+ *  - q and k may be rotated by a normalized Walsh-Hadamard transform, which keeps
+ *    q.k unchanged ("The Asymmetric Key-Value Cache Compression Framework",
+ *    Method; "Read What Matters", the Dual-QK abstract).
+ *
+ * Exact formulas fixed by this library where the pages are silent:
+ *  - quantizer (fp32): s32 = (max - min) / (2^b - 1); s = fp16(s32) and
+ *    z = fp16(min) are stored; code = clamp(rint_half_even((x - z) * (1 / s)),
+ *    0, 2^b - 1) with every operation rounded to fp32; s == 0 gives all-zero codes;
+ *  - residual rule: after every append, Q = G * floor(max(0, T - R) / G) tokens
+ *    are quantized and tokens [Q, T) stay FP16 (R to R + G - 1 of them);
+ *  - rotation: natural-order butterflies in fp32, then a multiply by
+ *    fp32(1/sqrt(128)); rotated keys are rounded to fp16 before storage, the
+ *    rotated query is kept in fp32, values are not rotated;
+ *  - attention: softmax(q.k * softmax_scale) over all T tokens of a sequence;
+ *    query head hq reads KV head hq / (num_q_heads / num_kv_heads).
+ *
+ * Conventions for every call:
+ *  - All functions have C linkage; no C++ exception crosses the ABI.
+ *  - Device pointers are plain device addresses (for example a torch tensor's
+ *    data_ptr()); host pointers are ordinary host memory. Callers own every
+ *    buffer they pass, and it must stay valid until the stream has passed the call.
+ *  - All argument checks run on the host before any launch; on any error the cache
+ *    state is unchanged and kvq_last_error() describes the problem.
+ *  - Calls are asynchronous on `stream` unless stated. A handle is not thread safe.
+ *  - Inputs holding NaN or Inf give undefined results (they are not scanned).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvq_cache kvq_cache; /* opaque, owned by the library */
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1, /* bad configuration, pointer, size or index */
+  KVQ_ERR_CAPACITY = -2,    /* an append would exceed max_tokens */
+  KVQ_ERR_OOM = -3,         /* device allocation failed or dev_bytes too small */
+  KVQ_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  KVQ_ERR_NO_DEVICE = -5,   /* no usable GPU (checked after argument validation) */
+  KVQ_ERR_EMPTY = -6        /* attention requested over a sequence with no tokens */
+} kvq_status;
+
+typedef struct {
+  int32_t batch;         /* B >= 1 sequences */
+  int32_t num_q_heads;   /* Hq; a multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* Hkv >= 1; Hq / Hkv must be 1, 2, 4 or 8 */
+  int32_t head_dim;      /* D; must be 128 */
+  int32_t bits;          /* 2 or 4 */
+  int32_t group;         /* G: tokens per key group = channels per value group; must be 32 */
+  int32_t residual;      /* R >= 0 and a multiple of G: FP16 window of the most recent tokens */
+  int32_t rotate;        /* 0 or 1: normalized Walsh-Hadamard transform on q and k */
+  int64_t max_tokens;    /* per-sequence capacity, 1 .. 2^30 */
+  float softmax_scale;   /* 0 => 1/sqrt(head_dim) */
+} kvq_config;
+
+/* Bytes of device memory a cache with this configuration needs (host only).
+ * Layout: per-sequence state, packed group blocks, FP16 residual rings, and the
+ * decode workspace, each 256-byte aligned. */
+kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes);
+
+/* Create a cache. If dev_mem is NULL the library allocates (and later frees) the
+ * memory; otherwise dev_mem must be a device buffer of at least kvq_cache_bytes()
+ * bytes, 256-byte aligned, owned by the caller and outliving the handle.
+ * The per-sequence state is cleared on `stream`. */
+kvq_status kvq_create(const kvq_config* cfg, void* dev_mem, size_t dev_bytes,
+                      hipStream_t stream, kvq_cache** out);
+
+/* Append tokens to every sequence.
+ *  k, v: device fp16 [B][n_max][Hkv][D], unrotated keys and values; row t of
+ *        sequence b is used for t < n_tokens[b].
+ *  n_tokens: host int32 [B] with 0 <= n_tokens[b] <= n_max, or NULL for n_max
+ *        tokens in every sequence.
+ * New keys are rotated when the cache rotates. Every group the residual rule moves
+ * out of the FP16 window is quantized and packed on the device; the tokens that
+ * stay FP16 are written to the window. k and v may be NULL when no token is
+ * appended. Errors: KVQ_ERR_CAPACITY if any sequence would exceed max_tokens. */
+kvq_status kvq_append(kvq_cache* c, const void* k, const void* v,
+                      const int32_t* n_tokens, int32_t n_max, hipStream_t stream);
+
+/* Decode-step attention of one query per head over every cached token.
+ *  q:   device fp16 [B][Hq][D] (unrotated; rotated in the kernel when the cache rotates)
+ *  out: device fp32 [B][Hq][D]
+ * The packed groups and the FP16 window are read once per KV head; the partial
+ * results of the sequence splits are merged in a second kernel.
+ * Errors: KVQ_ERR_EMPTY if any sequence holds no token. */
+kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, hipStream_t stream);
+
+/* Override the number of 32-token groups one workgroup of the decode kernel
+ * reads (0 restores the automatic choice). Must be 0 or in [4, 1 << 20]. */
+kvq_status kvq_set_decode_split(kvq_cache* c, int32_t groups_per_split);
+
+/* Record `start` before and `stop` after the decode split kernel on the stream
+ * passed to every later kvq_decode_attention call (both NULL to stop). Lets a
+ * caller time that kernel alone with hipEventElapsedTime. The events are owned by
+ * the caller; the library only records them. */
+kvq_status kvq_set_profile_events(kvq_cache* c, hipEvent_t start, hipEvent_t stop);
+
+/* Destroy a handle (NULL is accepted). Synchronizes the creation stream first and
+ * frees library-allocated memory. */
+void kvq_destroy(kvq_cache* c);
+
+/* Host mirror of sequence b: T = tokens appended, Q = tokens held quantized. */
+kvq_status kvq_seq_len(const kvq_cache* c, int32_t b, int64_t* T, int64_t* Q);
+
+/* Parts of the state that kvq_read_state can copy out. */
+enum {
+  KVQ_PART_GROUPS = 0, /* packed group blocks of (b, h): group g at byte g * kvq_group_bytes() */
+  KVQ_PART_RING_K = 1, /* FP16 key window of (b, h): [R + G][D], token t in slot t % (R + G) */
+  KVQ_PART_RING_V = 2  /* FP16 value window of (b, h), same layout */
+};
+
+/* Bytes of one packed 32-token group block: 3072 at 2 bits, 5120 at 4 bits.
+ * Block layout (little-endian): [key codes | value codes | key scale fp16[128] |
+ * key zero fp16[128] | value scales fp16[128] | value zeros fp16[128]].
+ * Code words: a code is addressed by (operand o in 0..7, lane l in 0..63,
+ * slot s in 0..7). Key token i, channel d: o = 2*(d/32) + i/16,
+ * l = i%16 + 16*((d%32)/8), s = d%8. Value token i, channel d: o = d/16,
+ * l = d%16 + 16*((i%16)/4), s = 4*(i/16) + i%4.
+ *   2-bit: 32-bit word at byte 16*l + 4*(o/2), bits from 8*(s/2) + 4*(s%2) + 2*(o%2);
+ *   4-bit: 32-bit word at byte 1024*(o/4) + 16*l + 4*(o%4), bits from 8*(s%4) + 4*(s/4).
+ * Value scale and zero of token i, channel group j sit at fp16 index
+ * (4*((i%16)/4) + j)*8 + 4*(i/16) + i%4 of their 128-entry arrays. */
+size_t kvq_group_bytes(int32_t bits);
+
+/* Copy `bytes` bytes of one part of (b, h) starting at byte `offset` to host_dst.
+ * Synchronizes `stream`. For test and inspection, not on the hot path. */
+kvq_status kvq_read_state(kvq_cache* c, int32_t part, int32_t b, int32_t h, size_t offset,
+                          void* host_dst, size_t bytes, hipStream_t stream);
+
+/* Message of the last error on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -10,17 +10,18 @@ the key outlier structure the pages describe: keys carry a few fixed
 large-magnitude channels, values show no channel structure ("KV cache
 quantization: putting the bits in the cached vectors", full-text-skim notes).
 
-Every tensor is generated per (tensor id, sequence, kv-head, 65,536-token chunk)
+Every tensor is generated per (tensor id, sequence, kv-head, 1,024-token chunk)
 from numpy's PCG64 seeded by SeedSequence([seed, tensor id, b, h, chunk]), so any
 token range of any head can be regenerated without materialising the rest.
 """
 from __future__ import annotations
 
 from dataclasses import dataclass, field, replace
+from functools import lru_cache
 
 import numpy as np
 
-CHUNK = 65536
+CHUNK = 1024
 HEAD_DIM = 128
 
 _TID_K, _TID_V, _TID_Q, _TID_OUTLIER, _TID_OFFSET, _TID_LENS = 0, 1, 2, 3, 4, 5
@@ -85,8 +86,11 @@ def key_channel_params(w: Workload, h: int):
     return mult, off
 
 
+@lru_cache(maxsize=2048)
 def _chunk_normals(w: Workload, tid: int, b: int, h: int, c: int) -> np.ndarray:
-    return _rng(w.seed, tid, b, h, c).standard_normal((CHUNK, w.head_dim), dtype=np.float32)
+    x = _rng(w.seed, tid, b, h, c).standard_normal((CHUNK, w.head_dim), dtype=np.float32)
+    x.flags.writeable = False
+    return x
 
 
 def _token_range(w: Workload, tid: int, b: int, h: int, t0: int, t1: int) -> np.ndarray:

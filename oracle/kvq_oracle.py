@@ -198,22 +198,40 @@ def _value_scale_index(i, j):
     return (kb * 4 + j) * 8 + slot
 
 
-def _pack_section(codes, coords_fn, bits, nbytes):
-    words = np.zeros(nbytes // 4, dtype=np.uint32)
+def _section_positions(coords_fn, bits):
+    """For every code (i, d) of a section: its 32-bit word index and bit offset."""
     ii, dd = np.meshgrid(np.arange(GROUP), np.arange(HEAD_DIM), indexing="ij")
     o, lane, slot = coords_fn(ii, dd)
     word, bit = _code_position(o, lane, slot, bits)
-    vals = codes.astype(np.uint32) << bit.astype(np.uint32)
-    np.bitwise_or.at(words, (word // 4).ravel(), vals.ravel())
+    return (word // 4).astype(np.int64), bit.astype(np.uint32)
+
+
+_POS_CACHE = {}
+
+
+def _positions(coords_fn, bits):
+    key = (coords_fn.__name__, bits)
+    if key not in _POS_CACHE:
+        _POS_CACHE[key] = _section_positions(coords_fn, bits)
+    return _POS_CACHE[key]
+
+
+def _pack_section(codes, coords_fn, bits, nbytes):
+    widx, bit = _positions(coords_fn, bits)
+    words = np.zeros(nbytes // 4, dtype=np.uint32)
+    np.bitwise_or.at(words, widx.ravel(), (codes.astype(np.uint32) << bit).ravel())
     return words
 
 
 def _unpack_section(words, coords_fn, bits):
-    ii, dd = np.meshgrid(np.arange(GROUP), np.arange(HEAD_DIM), indexing="ij")
-    o, lane, slot = coords_fn(ii, dd)
-    word, bit = _code_position(o, lane, slot, bits)
+    widx, bit = _positions(coords_fn, bits)
     mask = np.uint32(2 ** bits - 1)
-    return ((words[word // 4] >> bit.astype(np.uint32)) & mask).astype(np.uint8)
+    return ((words[widx] >> bit) & mask).astype(np.uint8)
+
+
+def _value_scale_indices():
+    ii, jj = np.meshgrid(np.arange(GROUP), np.arange(HEAD_DIM // GROUP), indexing="ij")
+    return _value_scale_index(ii, jj)
 
 
 def pack_group_block(kc, ks, kz, vc, vs, vz, bits):
@@ -226,13 +244,11 @@ def pack_group_block(kc, ks, kz, vc, vs, vz, bits):
     cb = GROUP * HEAD_DIM * bits // 8
     kw = _pack_section(kc, _key_code_coords, bits, cb)
     vw = _pack_section(vc, _value_code_coords, bits, cb)
+    idx = _value_scale_indices()
     vs_arr = np.zeros(128, dtype=_F16)
     vz_arr = np.zeros(128, dtype=_F16)
-    for i in range(GROUP):
-        for j in range(HEAD_DIM // GROUP):
-            idx = _value_scale_index(i, j)
-            vs_arr[idx] = vs[i, j]
-            vz_arr[idx] = vz[i, j]
+    vs_arr[idx] = vs
+    vz_arr[idx] = vz
     out = b"".join([
         kw.astype("<u4").tobytes(),
         vw.astype("<u4").tobytes(),
@@ -257,13 +273,9 @@ def unpack_group_block(block, bits):
     vz_arr = block[2 * cb + 768:2 * cb + 1024].view("<f2")
     kc = _unpack_section(kw, _key_code_coords, bits)
     vc = _unpack_section(vw, _value_code_coords, bits)
-    vs = np.zeros((GROUP, HEAD_DIM // GROUP), dtype=_F16)
-    vz = np.zeros((GROUP, HEAD_DIM // GROUP), dtype=_F16)
-    for i in range(GROUP):
-        for j in range(HEAD_DIM // GROUP):
-            idx = _value_scale_index(i, j)
-            vs[i, j] = vs_arr[idx]
-            vz[i, j] = vz_arr[idx]
+    idx = _value_scale_indices()
+    vs = vs_arr[idx].astype(_F16)
+    vz = vz_arr[idx].astype(_F16)
     return kc, ks, kz, vc, vs, vz
 
 

@@ -1,0 +1,88 @@
+"""C-ABI checks that need no GPU: exported symbols, host-side validation, layout sizes."""
+import ctypes
+import re
+import os
+
+import pytest
+
+import bit_asymmetric_kv_amd as kvq
+from bit_asymmetric_kv_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = kvq.load()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in kvq.h but not exported"
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_group_bytes():
+    assert kvq.group_bytes(2) == 3072
+    assert kvq.group_bytes(4) == 5120
+    assert kvq.group_bytes(3) == 0
+
+
+def _status(cfg):
+    lib = kvq.load()
+    h = ctypes.c_void_p(0)
+    s = lib.kvq_create(ctypes.byref(cfg), None, 0, None, ctypes.byref(h))
+    return s, lib.kvq_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value", [
+    ("batch", 0), ("num_kv_heads", 0), ("num_q_heads", 12), ("head_dim", 64), ("bits", 3), ("bits", 8),
+    ("group", 64), ("residual", 48), ("residual", -32), ("rotate", 2), ("max_tokens", 0),
+    ("max_tokens", 1 << 31), ("softmax_scale", -1.0), ("softmax_scale", float("inf")),
+])
+def test_invalid_configs_rejected_before_any_device_call(field, value):
+    cfg = kvq.make_config(2, 32, 8, residual=128, max_tokens=1000)
+    setattr(cfg, field, value)
+    s, msg = _status(cfg)
+    assert s == _lib.KVQ_ERR_INVALID_ARG, (field, value, s, msg)
+    assert msg
+
+
+def test_gqa_ratio_16_rejected():
+    cfg = kvq.make_config(1, 32, 2)
+    assert _status(cfg)[0] == _lib.KVQ_ERR_INVALID_ARG
+
+
+def test_valid_config_reports_no_device_here_or_succeeds():
+    import torch
+    cfg = kvq.make_config(1, 8, 8, residual=32, max_tokens=100)
+    s, _ = _status(cfg)
+    if torch.cuda.is_available():
+        assert s == _lib.KVQ_OK
+    else:
+        assert s == _lib.KVQ_ERR_NO_DEVICE
+
+
+def test_null_arguments():
+    lib = kvq.load()
+    assert lib.kvq_append(None, None, None, None, 0, None) == _lib.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_decode_attention(None, None, None, None) == _lib.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_seq_len(None, 0, None, None) == _lib.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_set_decode_split(None, 0) == _lib.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_read_state(None, 0, 0, 0, 0, None, 0, None) == _lib.KVQ_ERR_INVALID_ARG
+    lib.kvq_destroy(None)
+    n = ctypes.c_size_t(0)
+    assert lib.kvq_cache_bytes(None, ctypes.byref(n)) == _lib.KVQ_ERR_INVALID_ARG
+
+
+def test_cache_bytes_grows_with_capacity_and_holds_the_blocks():
+    small = kvq.cache_bytes(kvq.make_config(1, 32, 8, residual=128, max_tokens=131072))
+    big = kvq.cache_bytes(kvq.make_config(1, 32, 8, residual=128, max_tokens=1 << 20))
+    assert big > small
+    # the packed store alone: 8 heads x 32768 groups x 3072 B = 768 MiB at 1M tokens
+    assert big >= 8 * 32768 * 3072
+    four = kvq.cache_bytes(kvq.make_config(1, 32, 8, bits=4, residual=128, max_tokens=131072))
+    assert four - small >= 8 * 4096 * (5120 - 3072)
