@@ -27,6 +27,8 @@ HIP_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no AGPR copies around the softmax rescale)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
 ]

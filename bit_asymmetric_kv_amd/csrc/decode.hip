@@ -46,7 +46,7 @@ struct DecodeArgs {
   const __half* q;
   float* part;
   long long gcap;
-  int Hkv, Hq, W, gps, nsplit, rotate;
+  int Hkv, Hq, W, gps, nsplit, ntail, rotate;  // nsplit quantized splits + ntail window chunks
   float scale_log2;
 };
 
@@ -91,27 +91,21 @@ __device__ inline half8 code_operand(const uint4& w0, const uint4& w1, int o) {
   }
 }
 
-// Value of the lane that holds the other (high or low) column of the same head.
-// Columns are laid out as head h high at u = h, low at u = U - 1 - h (u = lane % U).
-template <int U>
-__device__ inline float partner(float x) {
-  int xi = __builtin_bit_cast(int, x);
-  int r;
-  if constexpr (U == 2) r = __builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
-  else if constexpr (U == 4) r = __builtin_amdgcn_update_dpp(0, xi, 0x1B, 0xF, 0xF, false);   // quad_perm 3,2,1,0
-  else if constexpr (U == 8) r = __builtin_amdgcn_update_dpp(0, xi, 0x141, 0xF, 0xF, false);  // row_half_mirror
-  else r = __builtin_amdgcn_update_dpp(0, xi, 0x140, 0xF, 0xF, false);                         // row_mirror
-  return __builtin_bit_cast(float, r);
-}
-
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
 __device__ inline float wave_max_rows(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  return fmaxf(x, __shfl_xor(x, 32));
 }
 __device__ inline float wave_sum_rows(float x) {
   x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
+  return x + __shfl_xor(x, 32);
+}
+
+// Sum over the four quads of a 16-lane row for lanes with equal lane % 4
+// (DPP row rotations by 4 and 8).
+__device__ inline float row_sum_stride4(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
   return x;
 }
 
@@ -161,18 +155,25 @@ __device__ void prepare_query(const DecodeArgs& a, int b, int h, float (*qf)[kD]
 
 // Partial of one query head: running max m (log2 domain), sum l, output o[128].
 __device__ inline float* partial_ptr(const DecodeArgs& a, int b, int hq, int split) {
-  return a.part + ((size_t(b) * a.Hq + hq) * size_t(a.nsplit + 1) + split) * kPartialStride;
+  return a.part + ((size_t(b) * a.Hq + hq) * size_t(a.nsplit + a.ntail) + split) * kPartialStride;
 }
 
-// Merge the per-wave partials held in shared memory (m, l, o per wave and head) and
-// write the workgroup's partial.
+// Per-wave partials (m, l, o[128] per head) in shared memory; wave w's block starts
+// at base + w * stride floats.
+struct WaveParts {
+  float* base;
+  int stride;
+  __device__ float& at(int w, int hh, int c) const { return base[w * stride + hh * kPartialStride + c]; }
+};
+
+// Merge the per-wave partials and write the workgroup's partial.
 template <int HG>
-__device__ void merge_and_store(const DecodeArgs& a, int b, int h, int split, float (*wp)[HG][kPartialStride]) {
+__device__ void merge_and_store(const DecodeArgs& a, int b, int h, int split, const WaveParts& wp) {
   __syncthreads();
   for (int idx = threadIdx.x; idx < HG * kPartialStride; idx += blockDim.x) {
     int hh = idx / kPartialStride, c = idx % kPartialStride;
     float M = -INFINITY;
-    for (int w = 0; w < kWaves; w++) M = fmaxf(M, wp[w][hh][0]);
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, wp.at(w, hh, 0));
     float r;
     if (c == 0) {
       r = M;
@@ -181,144 +182,209 @@ __device__ void merge_and_store(const DecodeArgs& a, int b, int h, int split, fl
     } else {
       r = 0.0f;
       for (int w = 0; w < kWaves; w++) {
-        float mw = wp[w][hh][0];
-        if (mw != -INFINITY) r += wp[w][hh][c] * exp2f(mw - M);
+        float mw = wp.at(w, hh, 0);
+        if (mw != -INFINITY) r += wp.at(w, hh, c) * exp2f(mw - M);
       }
     }
     partial_ptr(a, b, h * HG + hh, split)[c] = r;
   }
 }
 
-// Attention over the FP16 window [Q, T) of one (kv-head, sequence), in chunks of
-// 256 tokens with a running max; the result goes to wave 0's slot of `wp`.
+// Attention over one 32-token chunk [t0, t0 + cnt) of the FP16 window of one
+// (kv-head, sequence); cnt may be 0. Scores: each wave takes 8 tokens, 8 lanes per
+// token each dotting 16 channels with every query head. Output: each thread
+// accumulates 2 channels over 8 tokens; the four token quarters are merged through
+// the per-wave partial slots of `wp` (all with the same max).
 template <int HG>
-__device__ void tail_attention(const DecodeArgs& a, int b, int h, int T, int Q, float (*qf)[kD],
-                               const float* expo, float (*ts)[256], float (*wp)[HG][kPartialStride]) {
-  constexpr int NOUT = (HG * kD + 255) / 256;
-  __shared__ float m_s[HG], l_s[HG], alpha_s[HG];
+__device__ void tail_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt, float (*qf)[kD], const float* expo,
+                           float (*ts)[kG], const WaveParts& wp) {
+  __shared__ float m_s[HG], l_s[HG];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const size_t bh = size_t(b) * a.Hkv + h;
-  if (tid < HG) {
-    m_s[tid] = -INFINITY;
-    l_s[tid] = 0.0f;
+  {
+    const int tl = wave * 8 + lane / 8, cs = lane % 8;
+    float acc[HG];
+    for (int hh = 0; hh < HG; hh++) acc[hh] = 0.0f;
+    if (tl < cnt) {
+      const uint8_t* krow =
+          reinterpret_cast<const uint8_t*>(a.ringk + (bh * a.W + size_t((t0 + tl) % a.W)) * kD) + 32 * cs;
+      const half8 k0 = load_half8(krow), k1 = load_half8(krow + 16);
+      for (int hh = 0; hh < HG; hh++) {
+        float x = 0.0f;
+        for (int s = 0; s < 8; s++) x = __builtin_fmaf(qf[hh][16 * cs + s], float(k0[s]), x);
+        for (int s = 0; s < 8; s++) x = __builtin_fmaf(qf[hh][16 * cs + 8 + s], float(k1[s]), x);
+        acc[hh] = x;
+      }
+    }
+    for (int hh = 0; hh < HG; hh++) {
+      float x = acc[hh];
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      if (cs == 0) ts[hh][tl] = tl < cnt ? x * expo[hh] : -INFINITY;
+    }
   }
-  float o[NOUT];
-  for (int r = 0; r < NOUT; r++) o[r] = 0.0f;
   __syncthreads();
-  for (int c0 = Q; c0 < T; c0 += 256) {
-    const int cnt = min(256, T - c0);
-    if (tid < cnt) {
-      const uint8_t* krow = reinterpret_cast<const uint8_t*>(a.ringk + (bh * a.W + size_t((c0 + tid) % a.W)) * kD);
-      float acc[HG];
-      for (int hh = 0; hh < HG; hh++) acc[hh] = 0.0f;
-      for (int d8 = 0; d8 < kD / 8; d8++) {
-        half8 kv = load_half8(krow + 16 * d8);
-        for (int s = 0; s < 8; s++)
-          for (int hh = 0; hh < HG; hh++) acc[hh] += qf[hh][8 * d8 + s] * float(kv[s]);
-      }
-      for (int hh = 0; hh < HG; hh++) ts[hh][tid] = acc[hh] * expo[hh];
-    } else {
-      for (int hh = 0; hh < HG; hh++) ts[hh][tid] = -INFINITY;
+  for (int hh = wave; hh < HG; hh += kWaves) {
+    float sc = lane < kG ? ts[hh][lane] : -INFINITY;
+    float m = sc;
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float p = (lane < cnt && m != -INFINITY) ? exp2f(sc - m) : 0.0f;
+    float l = p;
+    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+    if (lane < kG) ts[hh][lane] = p;
+    if (lane == 0) {
+      m_s[hh] = m;
+      l_s[hh] = l;
     }
-    __syncthreads();
-    for (int hh = wave; hh < HG; hh += kWaves) {
-      float m = -INFINITY;
-      for (int t = lane; t < 256; t += 64) m = fmaxf(m, ts[hh][t]);
-      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      const float m_old = m_s[hh];
-      const float m_new = fmaxf(m_old, m);
-      float sum = 0.0f;
-      for (int t = lane; t < 256; t += 64) {
-        float p = t < cnt ? exp2f(ts[hh][t] - m_new) : 0.0f;
-        ts[hh][t] = p;
-        sum += p;
-      }
-      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-      if (lane == 0) {
-        const float alpha = m_old == -INFINITY ? 0.0f : exp2f(m_old - m_new);
-        alpha_s[hh] = alpha;
-        l_s[hh] = l_s[hh] * alpha + sum;
-        m_s[hh] = m_new;
-      }
-    }
-    __syncthreads();
-    for (int r = 0; r < NOUT; r++) {
-      const int idx = tid + 256 * r;
-      if (idx < HG * kD) {
-        const int hh = idx / kD, d = idx % kD;
-        float acc = o[r] * alpha_s[hh];
-        for (int t = 0; t < cnt; t++)
-          acc += ts[hh][t] * __half2float(a.ringv[(bh * a.W + size_t((c0 + t) % a.W)) * kD + d]);
-        o[r] = acc;
-      }
-    }
-    __syncthreads();
   }
-  for (int r = 0; r < NOUT; r++) {
-    const int idx = tid + 256 * r;
-    if (idx < HG * kD) wp[0][idx / kD][2 + idx % kD] = o[r];
+  __syncthreads();
+  {
+    const int d2 = tid % 64, tq = tid / 64;
+    float o0[HG], o1[HG];
+    for (int hh = 0; hh < HG; hh++) o0[hh] = o1[hh] = 0.0f;
+    for (int j = 0; j < 8; j++) {
+      const int tl = 8 * tq + j;
+      if (tl < cnt) {
+        const __half2 vv =
+            *reinterpret_cast<const __half2*>(a.ringv + (bh * a.W + size_t((t0 + tl) % a.W)) * kD + 2 * d2);
+        const float v0 = __low2float(vv), v1 = __high2float(vv);
+        for (int hh = 0; hh < HG; hh++) {
+          o0[hh] = __builtin_fmaf(ts[hh][tl], v0, o0[hh]);
+          o1[hh] = __builtin_fmaf(ts[hh][tl], v1, o1[hh]);
+        }
+      }
+    }
+    for (int hh = 0; hh < HG; hh++) {
+      wp.at(tq, hh, 2 + 2 * d2) = o0[hh];
+      wp.at(tq, hh, 3 + 2 * d2) = o1[hh];
+    }
+    if (tid < HG * kWaves) {
+      const int hh = tid % HG, w = tid / HG;
+      wp.at(w, hh, 0) = m_s[hh];
+      wp.at(w, hh, 1) = w == 0 ? l_s[hh] : 0.0f;
+    }
   }
-  if (tid < HG) {
-    wp[0][tid][0] = m_s[tid];
-    wp[0][tid][1] = l_s[tid];
-    for (int w = 1; w < kWaves; w++) wp[w][tid][0] = -INFINITY;
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this
+// wave are outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int LPG, int NBUF>
+__device__ __forceinline__ void wait_group_loads(int outstanding_groups) {
+  // outstanding_groups is in [0, NBUF - 2]; each group is LPG load instructions.
+  if (outstanding_groups <= 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  else if (NBUF > 2 && outstanding_groups == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPG));
+  else if (NBUF > 3 && outstanding_groups == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPG));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF > 4 ? 3 : 0) * LPG));
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The bytes of one group block that a lane uses, read from the wave's shared-memory
+// copy of the block.
+template <int BITS, int NJ>
+struct GroupRegs {
+  uint4 kc0, kc1, vc0, vc1;  // key / value code words (kc1, vc1 used at 4 bits)
+  half8 ks, kz;              // key scale / zero of this lane's 8-channel block
+  half8 vs[NJ], vz[NJ];      // value scale / zero of this lane's 8 tokens per channel group
+};
+
+template <int BITS, int NJ>
+__device__ __forceinline__ void read_group(GroupRegs<BITS, NJ>& G, const uint8_t* blk, int lane, int cb, int kb,
+                                           int jbase) {
+  constexpr int CB = kG * kD * BITS / 8;
+  G.kc0 = *reinterpret_cast<const uint4*>(blk + 16 * lane);
+  G.vc0 = *reinterpret_cast<const uint4*>(blk + CB + 16 * lane);
+  if constexpr (BITS == 4) {
+    G.kc1 = *reinterpret_cast<const uint4*>(blk + 1024 + 16 * lane);
+    G.vc1 = *reinterpret_cast<const uint4*>(blk + CB + 1024 + 16 * lane);
+  }
+  G.ks = load_half8(blk + 2 * CB + 16 * cb);
+  G.kz = load_half8(blk + 2 * CB + 256 + 16 * cb);
+  for (int jr = 0; jr < NJ; jr++) {
+    G.vs[jr] = load_half8(blk + 2 * CB + 512 + 16 * (kb * 4 + jbase + jr));
+    G.vz[jr] = load_half8(blk + 2 * CB + 768 + 16 * (kb * 4 + jbase + jr));
   }
 }
 
 template <int BITS, int HG>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-  constexpr int U = 2 * HG;                   // useful MFMA columns: high and low part per head
-  constexpr int REP = 16 / U;                 // replicas of those columns across the 16 columns
+  // MFMA columns: one per query head of the kv-head, replicated REP times over the
+  // 16 columns. The fp16 high and low parts of each B operand go through two MFMAs
+  // into the same accumulator.
+  constexpr int REP = 16 / HG;
   constexpr int NJ = REP >= 4 ? 1 : 4 / REP;  // value channel groups handled per lane
-  constexpr int CB = kG * kD * BITS / 8;      // bytes of one code section
-  constexpr int GB = 2 * CB + 1024;           // bytes of one group block
+  constexpr int GB = 2 * (kG * kD * BITS / 8) + 1024;
+  constexpr int LPG = GB / 1024;              // 16-byte-per-lane loads per group block
+  constexpr int NBUF = 3;                     // group blocks per wave in shared memory
   constexpr int ITEMS = (HG + 3) / 4;         // key-side operand items per lane
 
+  // Each wave streams its group blocks HBM -> shared memory with direct loads into a
+  // ring of NBUF blocks; after the loop the same bytes hold the wave's partial.
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][NBUF * GB];
   __shared__ float qf[HG][kD];
   __shared__ float expo[HG];
   __shared__ union {
-    half8 bk[kWaves][4][U][4];  // key-side B operands per wave: [kc][column][k-block]
-    float ts[HG][256];          // FP16-window scores
+    struct {
+      half8 hi[4][HG][4];  // key-side B operands per wave: [kc][head][k-block]
+      half8 lo[4][HG][4];
+    } bk[kWaves];
+    float ts[HG][kG];  // FP16-window scores / weights of one chunk
   } sh;
-  __shared__ float wp[kWaves][HG][kPartialStride];
+  static_assert(NBUF * GB >= HG * kPartialStride * 4, "wave partial must fit in the wave's ring");
+  const WaveParts wp{reinterpret_cast<float*>(&ring[0][0]), NBUF * GB / 4};
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const SeqDesc sd = a.seq[b];
   const int T = sd.t_old + sd.n_new, Q = sd.q_new;
   const int ng = Q / kG;
+  const bool tail = split >= a.nsplit;
+
+  // This wave's groups.
+  const int g0 = split * a.gps;
+  const int g1 = min(ng, g0 + a.gps);
+  const int len = tail ? 0 : max(0, g1 - g0);
+  const int per = (len + kWaves - 1) / kWaves;
+  const int wg0 = g0 + wave * per;
+  const int wg1 = min(g1, wg0 + per);
+  const int n = tail ? 0 : max(0, wg1 - wg0);
+
+  const uint8_t* base = a.blocks + (size_t(b) * a.Hkv + h) * size_t(a.gcap) * GB;
+  uint8_t* myring = &ring[wave][0];
+  auto issue = [&](int r) {  // group wg0 + r into ring slot r % NBUF
+    const uint8_t* src = base + size_t(wg0 + r) * GB + 16 * lane;
+    uint8_t* dst = myring + (r % NBUF) * GB;
+    for (int i = 0; i < LPG; i++) __builtin_amdgcn_global_load_lds(src + 1024 * i, dst + 1024 * i, 16, 0, 0);
+  };
+  // Start streaming before the query preparation so that the two overlap.
+  for (int r = 0; r < NBUF - 1 && r < n; r++) issue(r);
 
   prepare_query<HG>(a, b, h, qf, expo);
 
-  if (split == a.nsplit) {
-    tail_attention<HG>(a, b, h, T, Q, qf, expo, sh.ts, wp);
+  if (tail) {
+    const int t0 = Q + kG * (split - a.nsplit);
+    tail_chunk<HG>(a, b, h, t0, max(0, min(kG, T - t0)), qf, expo, sh.ts, wp);
     merge_and_store<HG>(a, b, h, split, wp);
     return;
   }
 
-  const int g0 = split * a.gps;
-  const int g1 = min(ng, g0 + a.gps);
-  const int len = max(0, g1 - g0);
-  const int per = (len + kWaves - 1) / kWaves;
-  const int wg0 = g0 + wave * per;
-  const int wg1 = min(g1, wg0 + per);
-
-  // MFMA lane roles: column n = lane % 16, k-block / row block kb = lane / 16.
-  const int n = lane % 16, kb = lane / 16;
-  const int u = n % U;
-  const bool ishi = u < HG;
-  const int hd = ishi ? u : U - 1 - u;  // query head of this lane's column
-  const int rho = n / U;                // replica index of this column
+  // MFMA lane roles: column n = lane % 16 (head n % HG, replica n / HG), k-block or
+  // row block kb = lane / 16.
+  const int col = lane % 16, kb = lane / 16;
+  const int hd = col % HG;
+  const int rho = col / HG;
   const int jbase = (rho % (4 / NJ)) * NJ;
+  // Key-side operand preparation: channel block cb = lane / 4 (8 channels) and head
+  // (lane % 4) % HG + 4 * it. With this mapping the q . z_key sum of a head ends up
+  // in exactly the lanes whose MFMA column belongs to that head.
+  const int cb = lane / 4, hh0 = (lane % 4) % HG;
+  const bool bwriter = (lane % 4) < HG;
 
-  // Key-side operand preparation: channel block cb (8 channels), heads hh0 + 4 * it.
-  const int cb = lane % 16, hh0 = lane / 16;
   float qreg[ITEMS][8];
   for (int it = 0; it < ITEMS; it++)
-    for (int s = 0; s < 8; s++) {
-      const int hh = hh0 + 4 * it;
-      qreg[it][s] = hh < HG ? qf[hh][8 * cb + s] : 0.0f;
-    }
+    for (int s = 0; s < 8; s++) qreg[it][s] = qf[hh0 + 4 * it][8 * cb + s];
   const float ex = expo[hd];
 
   float4v oacc[8];
@@ -327,134 +393,144 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   float zacc[NJ];
   for (int jr = 0; jr < NJ; jr++) zacc[jr] = 0.0f;
 
-  const uint8_t* base = a.blocks + (size_t(b) * a.Hkv + h) * size_t(a.gcap) * GB;
-  for (int g = wg0; g < wg1; g++) {
-    const uint8_t* blk = base + size_t(g) * GB;
-    const uint4 kc0 = *reinterpret_cast<const uint4*>(blk + 16 * lane);
-    const uint4 kc1 = BITS == 4 ? *reinterpret_cast<const uint4*>(blk + 1024 + 16 * lane) : kc0;
-    const uint4 vc0 = *reinterpret_cast<const uint4*>(blk + CB + 16 * lane);
-    const uint4 vc1 = BITS == 4 ? *reinterpret_cast<const uint4*>(blk + CB + 1024 + 16 * lane) : vc0;
-    const half8 ks8 = load_half8(blk + 2 * CB + 16 * cb);
-    const half8 kz8 = load_half8(blk + 2 * CB + 256 + 16 * cb);
-    half8 vs8[NJ], vz8[NJ];
-    for (int jr = 0; jr < NJ; jr++) {
-      const int j = jbase + jr;
-      vs8[jr] = load_half8(blk + 2 * CB + 512 + 16 * (kb * 4 + j));
-      vz8[jr] = load_half8(blk + 2 * CB + 768 + 16 * (kb * 4 + j));
-    }
+  // The group loop is software-pipelined: while group r's softmax and value side run,
+  // group r+1's bytes are read from shared memory and its key-side scores computed,
+  // so the two dependency chains overlap.
+  GroupRegs<BITS, NJ> G;   // group whose scores are in s0 / s1
+  float4v s0, s1;
 
-    // q' = q * s_key (per channel) as fp16 high + low parts; q.z_key per head.
+  auto key_side = [&](const GroupRegs<BITS, NJ>& g, float4v& r0, float4v& r1) {
+    // q' = q * s_key per channel as fp16 high + low parts, through shared memory into
+    // the MFMA B layout; q . z_key per head.
     float qz[ITEMS];
     for (int it = 0; it < ITEMS; it++) {
       const int hh = hh0 + 4 * it;
       half8 hi, lo;
       float z = 0.0f;
       for (int s = 0; s < 8; s++) {
-        const float qp = qreg[it][s] * float(ks8[s]);
-        const _Float16 hv = _Float16(qp);
+        const _Float16 hv = _Float16(qreg[it][s] * float(g.ks[s]));
         hi[s] = hv;
-        lo[s] = _Float16(qp - float(hv));
-        z += qreg[it][s] * float(kz8[s]);
+        lo[s] = _Float16(__builtin_fmaf(qreg[it][s], float(g.ks[s]), -float(hv)));
+        z = __builtin_fmaf(qreg[it][s], float(g.kz[s]), z);
       }
-      for (int off = 1; off < 16; off <<= 1) z += __shfl_xor(z, off);
-      qz[it] = z;
-      if (hh < HG) {
-        sh.bk[wave][cb / 4][hh][cb % 4] = hi;
-        sh.bk[wave][cb / 4][U - 1 - hh][cb % 4] = lo;
+      qz[it] = wave_sum_rows(row_sum_stride4(z));
+      if (bwriter) {
+        sh.bk[wave].hi[cb / 4][hh][cb % 4] = hi;
+        sh.bk[wave].lo[cb / 4][hh][cb % 4] = lo;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float qzc;
-    if constexpr (ITEMS == 1) {
-      qzc = __shfl(qz[0], 16 * (hd % 4));
-    } else {
-      const float q0 = __shfl(qz[0], 16 * (hd % 4));
-      const float q1 = __shfl(qz[1], 16 * (hd % 4));
-      qzc = hd >= 4 ? q1 : q0;
-    }
-    const float init = ishi ? qzc : 0.0f;
-
-    // Scores of the group's 32 tokens: rows 4*kb + i of tiles 0 and 1.
-    float4v s0 = {init, init, init, init}, s1 = s0;
+    if constexpr (ITEMS == 1) qzc = qz[0];
+    else qzc = hd >= 4 ? qz[1] : qz[0];
+    // Scores of the group's 32 tokens: rows 4*kb + i of token tiles 0 and 1.
+    r0 = float4v{qzc, qzc, qzc, qzc};
+    r1 = r0;
     for (int kc = 0; kc < 4; kc++) {
-      const half8 bk = sh.bk[wave][kc][u][kb];
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(kc0, kc1, 2 * kc), bk, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(kc0, kc1, 2 * kc + 1), bk, s1, 0, 0, 0);
+      const half8 bh = sh.bk[wave].hi[kc][hd][kb];
+      const half8 bl = sh.bk[wave].lo[kc][hd][kb];
+      const half8 a0 = code_operand<BITS>(g.kc0, g.kc1, 2 * kc);
+      const half8 a1 = code_operand<BITS>(g.kc0, g.kc1, 2 * kc + 1);
+      r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bh, r0, 0, 0, 0);
+      r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bh, r1, 0, 0, 0);
+      r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bl, r0, 0, 0, 0);
+      r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bl, r1, 0, 0, 0);
     }
-    float sc[8];
-    for (int i = 0; i < 4; i++) {
-      sc[i] = (s0[i] + partner<U>(s0[i])) * ex;
-      sc[4 + i] = (s1[i] + partner<U>(s1[i])) * ex;
-    }
+  };
 
-    // Online softmax (log2 domain), shared by every lane of the head.
-    float mloc = sc[0];
-    for (int i = 1; i < 8; i++) mloc = fmaxf(mloc, sc[i]);
+  auto value_side = [&](const GroupRegs<BITS, NJ>& g, const float4v& r0, const float4v& r1) {
+    const float sc[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    // Online softmax. Scores stay in the prescaled units S (log2 units are ex * S);
+    // the running max m_run is kept in the same units.
+    float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mloc = wave_max_rows(mloc);
     const float m_new = fmaxf(m_run, mloc);
     if (__ballot(m_new > m_run)) {
-      const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
+      const float alpha = m_run == -INFINITY ? 0.0f : exp2f(ex * (m_run - m_new));
       for (int t = 0; t < 8; t++) oacc[t] *= alpha;
       l_run *= alpha;
       for (int jr = 0; jr < NJ; jr++) zacc[jr] *= alpha;
       m_run = m_new;
     }
+    const float negm = -ex * m_run;
     float p[8];
     for (int i = 0; i < 8; i++) {
-      p[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
+      p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], ex, negm));
       l_run += p[i];
     }
-
-    // Value side: B = p * s_value (high or low part by column), plus sum p * z.
-    half8 bv[NJ];
+    // Value side: B = p * s_value (fp16 high + low parts), plus sum p * z_value.
+    half8 bvh[NJ], bvl[NJ];
     for (int jr = 0; jr < NJ; jr++) {
       float z = zacc[jr];
       for (int s = 0; s < 8; s++) {
-        const float pp = p[s] * float(vs8[jr][s]);
-        const _Float16 hv = _Float16(pp);
-        bv[jr][s] = ishi ? hv : _Float16(pp - float(hv));
-        z += p[s] * float(vz8[jr][s]);
+        const _Float16 hv = _Float16(p[s] * float(g.vs[jr][s]));
+        bvh[jr][s] = hv;
+        bvl[jr][s] = _Float16(__builtin_fmaf(p[s], float(g.vs[jr][s]), -float(hv)));
+        z = __builtin_fmaf(p[s], float(g.vz[jr][s]), z);
       }
       zacc[jr] = z;
     }
-    for (int t = 0; t < 8; t++)
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(vc0, vc1, t), bv[(t / 2) % NJ], oacc[t],
-                                                       0, 0, 0);
-  }
+    for (int t = 0; t < 8; t++) {
+      const half8 av = code_operand<BITS>(g.vc0, g.vc1, t);
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bvh[(t / 2) % NJ], oacc[t], 0, 0, 0);
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bvl[(t / 2) % NJ], oacc[t], 0, 0, 0);
+    }
+  };
 
-  // Wave partial: sums over the four row blocks, high + low columns.
+  if (n > 0) {
+    // Group r has landed once at most min(NBUF - 2, n - 1 - r) later groups are still
+    // in flight; after reading it, the slot read one iteration earlier is refilled.
+    wait_group_loads<LPG, NBUF>(min(NBUF - 2, n - 1));
+    read_group<BITS, NJ>(G, myring, lane, cb, kb, jbase);
+    if (NBUF - 1 < n) issue(NBUF - 1);
+    key_side(G, s0, s1);
+  }
+  for (int r = 0; r + 1 < n; r++) {
+    GroupRegs<BITS, NJ> Gn;
+    wait_group_loads<LPG, NBUF>(min(NBUF - 2, n - 2 - r));
+    read_group<BITS, NJ>(Gn, myring + ((r + 1) % NBUF) * GB, lane, cb, kb, jbase);
+    if (r + NBUF < n) issue(r + NBUF);
+    value_side(G, s0, s1);
+    key_side(Gn, s0, s1);
+    G = Gn;
+  }
+  if (n > 0) value_side(G, s0, s1);
+
+  // Wave partial: sums over the four row blocks, written over this wave's ring (all
+  // of its loads have completed).
   const float l_tot = wave_sum_rows(l_run);
   float zs[NJ];
   for (int jr = 0; jr < NJ; jr++) zs[jr] = wave_sum_rows(zacc[jr]);
-  if (kb == 0 && ishi && rho == 0) {
-    wp[wave][hd][0] = m_run;
-    wp[wave][hd][1] = l_tot;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if (kb == 0 && rho == 0) {
+    wp.at(wave, hd, 0) = m_run == -INFINITY ? -INFINITY : ex * m_run;
+    wp.at(wave, hd, 1) = l_tot;
   }
   for (int t = 0; t < 8; t++) {
-    const int valid_rho = (t / 2) / NJ;
-    for (int i = 0; i < 4; i++) {
-      const float v = oacc[t][i] + partner<U>(oacc[t][i]);
-      if (ishi && rho == valid_rho) wp[wave][hd][2 + 16 * t + 4 * kb + i] = v + zs[(t / 2) % NJ];
-    }
+    if (rho == (t / 2) / NJ)
+      for (int i = 0; i < 4; i++) wp.at(wave, hd, 2 + 16 * t + 4 * kb + i) = oacc[t][i] + zs[(t / 2) % NJ];
   }
   merge_and_store<HG>(a, b, h, split, wp);
 }
 
-// out[b][hq] = sum_i o_i 2^(m_i - M) / sum_i l_i 2^(m_i - M) over the partials of
-// one (sequence, query head). 512 threads: the partials' weights are computed once
-// into shared memory, then 4 slices of 128 threads (one per channel) sum strided
-// subsets of the partials and are added at the end.
-constexpr int kCombineThreads = 512;
-constexpr int kCombineMaxParts = kMaxSplits + 1;
+// out[b][hq][d] = sum_i o_i[d] 2^(m_i - M) / sum_i l_i 2^(m_i - M) over the
+// partials of one (sequence, query head). One workgroup per (query head, sequence,
+// 16-channel slice): the weights 2^(m_i - M) go to shared memory once, then 16
+// slices of 16 threads sum strided subsets of the partials.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineChannels = 16;
+constexpr int kCombineMaxParts = kMaxSplits + kMaxResidual / kGroup + 1;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part,
                                                                   float* __restrict__ out, int Hq, int nparts) {
   __shared__ float wgt[kCombineMaxParts];
   __shared__ float red[kCombineThreads / 64];
-  __shared__ float osum[kCombineThreads / kD][kD];
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  __shared__ float osum[kCombineThreads / kCombineChannels][kCombineChannels];
+  const int hq = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z * kCombineChannels, tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
   const float* p = part + (size_t(b) * Hq + hq) * size_t(nparts) * kPartialStride;
 
@@ -480,25 +556,25 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   float L = 0.0f;
   for (int w = 0; w < kCombineThreads / 64; w++) L += red[w];
 
-  const int d = tid % kD, slice = tid / kD;
-  constexpr int kSlices = kCombineThreads / kD;
+  constexpr int kSlices = kCombineThreads / kCombineChannels;
+  const int dl = tid % kCombineChannels, slice = tid / kCombineChannels;
   float o = 0.0f;
   for (int i = slice; i < nparts; i += kSlices) {
     const float wi = wgt[i];
-    if (wi != 0.0f) o += wi * p[size_t(i) * kPartialStride + 2 + d];
+    if (wi != 0.0f) o += wi * p[size_t(i) * kPartialStride + 2 + d0 + dl];
   }
-  osum[slice][d] = o;
+  osum[slice][dl] = o;
   __syncthreads();
   if (slice == 0) {
     float acc = 0.0f;
-    for (int s2 = 0; s2 < kSlices; s2++) acc += osum[s2][d];
-    out[(size_t(b) * Hq + hq) * kD + d] = acc / L;
+    for (int s2 = 0; s2 < kSlices; s2++) acc += osum[s2][dl];
+    out[(size_t(b) * Hq + hq) * kD + d0 + dl] = acc / L;
   }
 }
 
 template <int BITS, int HG>
 hipError_t launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<BITS, HG>), dim3(a.nsplit + 1, a.Hkv, B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<BITS, HG>), dim3(a.nsplit + a.ntail, a.Hkv, B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -520,6 +596,7 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   a.W = L.W;
   a.gps = groups_per_split;
   a.nsplit = nsplit;
+  a.ntail = L.R / kG + 1;
   a.rotate = rotate;
   a.scale_log2 = scale_log2;
   const int hg = L.Hq / L.Hkv;
@@ -538,7 +615,7 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   }
   if (e != hipSuccess) return e;
   if (prof_stop && hipEventRecord(prof_stop, stream) != hipSuccess) return hipGetLastError();
-  hipLaunchKernelGGL(combine_kernel, dim3(L.Hq, L.B), dim3(kCombineThreads), 0, stream, a.part, out, L.Hq, nsplit + 1);
+  hipLaunchKernelGGL(combine_kernel, dim3(L.Hq, L.B, kD / kCombineChannels), dim3(kCombineThreads), 0, stream, a.part, out, L.Hq, a.nsplit + a.ntail);
   return hipGetLastError();
 }
 

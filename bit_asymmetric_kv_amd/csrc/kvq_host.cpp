@@ -60,7 +60,7 @@ kvq_status validate(const kvq_config* cfg) {
     return fail(KVQ_ERR_INVALID_ARG, "group must be 32 (got %d)", cfg->group);
   if (cfg->head_dim % cfg->group)
     return fail(KVQ_ERR_INVALID_ARG, "head_dim must be a multiple of group");
-  if (cfg->residual < 0 || cfg->residual % cfg->group || cfg->residual > 4096)
+  if (cfg->residual < 0 || cfg->residual % cfg->group || cfg->residual > kvq::kMaxResidual)
     return fail(KVQ_ERR_INVALID_ARG, "residual must be a multiple of group in [0, 4096] (got %d)",
                 cfg->residual);
   if (cfg->rotate != 0 && cfg->rotate != 1) return fail(KVQ_ERR_INVALID_ARG, "rotate must be 0 or 1");
@@ -94,7 +94,7 @@ Layout make_layout(const kvq_config* cfg) {
   L.ringv_off = off;
   off = align256(off + ring);
   L.part_off = off;
-  off = align256(off + size_t(L.B) * L.Hq * size_t(L.max_splits + 1) * kvq::kPartialStride * 4);
+  off = align256(off + size_t(L.B) * L.Hq * size_t(L.max_splits + L.R / kvq::kGroup + 1) * kvq::kPartialStride * 4);
   L.total = off;
   return L;
 }

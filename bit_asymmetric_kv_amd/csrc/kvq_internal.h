@@ -11,6 +11,7 @@ constexpr int kGroup = 32;
 constexpr int kPartialStride = kHeadDim + 2;  // m (log2 domain), l, o[128] per partial
 constexpr int kMinGroupsPerSplit = 4;
 constexpr int kMaxSplits = 2048;
+constexpr int kMaxResidual = 4096;  // FP16 window chunks: residual / 32 + 1 per (b, h)
 
 // Per-sequence record kept on the device and rewritten by every append:
 // tokens before the append, tokens appended, quantized tokens before and after.
