@@ -146,6 +146,8 @@ def main():
     ap.add_argument("--copies", type=int, default=8, help="independent caches stepped round-robin")
     ap.add_argument("--groups-per-split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-iters", type=int, default=30,
+                    help="extra decode calls on one cache to report a last-level-cache-resident time (0: skip)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters, if present")
     args = ap.parse_args()
@@ -212,13 +214,14 @@ def main():
     # warm (last-level-cache resident) decode of one cache, for reference only
     c = caches[0]
     qw = q[0].contiguous()
-    wst, wen = ev.create(30), ev.create(30)
-    for i in range(30):
+    nw = max(0, args.warm_iters)
+    wst, wen = ev.create(nw), ev.create(nw)
+    for i in range(nw):
         ev.record(wst[i], stream)
         c.decode(qw, outs[0])
         ev.record(wen[i], stream)
     torch.cuda.synchronize()
-    warm = [ev.elapsed_ms(wst[i], wen[i]) for i in range(10, 30)]
+    warm = [ev.elapsed_ms(wst[i], wen[i]) for i in range(nw // 3, nw)] or [float("nan")]
     for e in (st, en, ks, ke, wst, wen):
         ev.destroy(e)
 

@@ -101,7 +101,7 @@ __device__ inline int value_token(int kb, int s) { return s < 4 ? 4 * kb + s : 1
 
 template <int BITS>
 __global__ __launch_bounds__(256) void flush_kernel(uint8_t* __restrict__ blocks, const __half* __restrict__ ringk,
-                                                    const __half* __restrict__ ringv, const SeqDesc* __restrict__ seq,
+                                                    const __half* __restrict__ ringv, const SeqArgs seq,
                                                     const __half* __restrict__ kin, const __half* __restrict__ vin,
                                                     int Hkv, int W, long long gcap, int n_max, int rotate) {
   constexpr int CB = kG * kD * BITS / 8;  // bytes of one code section
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void flush_kernel(uint8_t* __restrict__ blocks
   __shared__ int from_input[kG];
 
   const int h = blockIdx.y, b = blockIdx.z;
-  const SeqDesc sd = seq[b];
+  const SeqDesc sd = seq.inl_valid ? seq.inl[b] : seq.dev[b];
   const int nflush = (sd.q_new - sd.q_old) / kG;
   if (int(blockIdx.x) >= nflush) return;
   const int g = sd.q_old / kG + blockIdx.x;
@@ -200,13 +200,14 @@ __global__ __launch_bounds__(256) void flush_kernel(uint8_t* __restrict__ blocks
 
 // One block per (appended token that stays in the FP16 window, kv-head, sequence).
 __global__ __launch_bounds__(128) void ring_write_kernel(__half* __restrict__ ringk, __half* __restrict__ ringv,
-                                                         const SeqDesc* __restrict__ seq, const __half* __restrict__ kin,
+                                                         const SeqArgs seq, const __half* __restrict__ kin,
                                                          const __half* __restrict__ vin, int Hkv, int W, int n_max,
                                                          int rotate) {
   __shared__ float row[kD];
   __shared__ int one;
   const int h = blockIdx.y, b = blockIdx.z;
-  const SeqDesc sd = seq[b];
+  const SeqDesc sd = seq.inl_valid ? seq.inl[b] : seq.dev[b];
+  if (seq.inl_valid && blockIdx.x == 0 && h == 0 && threadIdx.x == 0) seq.state[b] = sd;
   const int t_new = sd.t_old + sd.n_new;
   const int first = max(sd.t_old, sd.q_new);
   const int t = first + blockIdx.x;
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(128) void ring_write_kernel(__half* __restrict__ ri
 
 }  // namespace
 
-hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* k, const void* v,
+hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqArgs& seq, const void* k, const void* v,
                         int32_t n_max, int32_t max_flush_groups, int rotate, hipStream_t stream) {
   dim3 grid(max_flush_groups, L.Hkv, L.B);
   auto* blocks = base + L.blocks_off;
@@ -245,7 +246,7 @@ hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqDesc* seq, cons
   return hipGetLastError();
 }
 
-hipError_t launch_ring_write(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* k, const void* v,
+hipError_t launch_ring_write(const Layout& L, uint8_t* base, const SeqArgs& seq, const void* k, const void* v,
                              int32_t n_max, int32_t max_ring_tokens, int rotate, hipStream_t stream) {
   dim3 grid(max_ring_tokens, L.Hkv, L.B);
   hipLaunchKernelGGL(ring_write_kernel, grid, dim3(kD), 0, stream, reinterpret_cast<__half*>(base + L.ringk_off),

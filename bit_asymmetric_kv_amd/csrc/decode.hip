@@ -46,7 +46,7 @@ struct DecodeArgs {
   const __half* q;
   float* part;
   long long gcap;
-  int Hkv, Hq, W, gps, nsplit, ntail, rotate;  // nsplit quantized splits + ntail window chunks
+  int B, Hkv, Hq, W, gps, nsplit, rotate;  // partials per query head: nsplit + 1 (FP16 window last)
   float scale_log2;
 };
 
@@ -91,6 +91,19 @@ __device__ inline half8 code_operand(const uint4& w0, const uint4& w1, int o) {
   }
 }
 
+// Value held by the lane of the paired column inside a block of U columns, for the
+// mirror layout u <-> U - 1 - u (u = lane % U) used to pair high and low parts.
+template <int U>
+__device__ inline float partner(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  int r;
+  if constexpr (U == 2) r = __builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
+  else if constexpr (U == 4) r = __builtin_amdgcn_update_dpp(0, xi, 0x1B, 0xF, 0xF, false);   // quad_perm 3,2,1,0
+  else if constexpr (U == 8) r = __builtin_amdgcn_update_dpp(0, xi, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  else r = __builtin_amdgcn_update_dpp(0, xi, 0x140, 0xF, 0xF, false);                         // row_mirror
+  return __builtin_bit_cast(float, r);
+}
+
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
 __device__ inline float wave_max_rows(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
@@ -101,12 +114,55 @@ __device__ inline float wave_sum_rows(float x) {
   return x + __shfl_xor(x, 32);
 }
 
+// Max over the four quads of a 16-lane row for lanes with equal lane % 4.
+__device__ inline float row_max_stride4(float x) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false)));
+  return x;
+}
+
 // Sum over the four quads of a 16-lane row for lanes with equal lane % 4
 // (DPP row rotations by 4 and 8).
 __device__ inline float row_sum_stride4(float x) {
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
   return x;
+}
+
+// Two fp16 products rounded once from fp32 operands and an fp16 pair:
+// r.lo = f16(a0 * s.lo), r.hi = f16(a1 * s.hi)  (v_fma_mixlo / v_fma_mixhi).
+__device__ inline uint32_t mul_to_f16x2(float a0, float a1, uint32_t s) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %3, 0 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mixhi_f16 %0, %2, %3, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+      : "=&v"(r)
+      : "v"(a0), "v"(a1), "v"(s));
+  return r;
+}
+// The low parts of the same products: r.lo = f16(a0 * s.lo - h.lo),
+// r.hi = f16(a1 * s.hi - h.hi), each fused and rounded once.
+__device__ inline uint32_t mul_residual_f16x2(float a0, float a1, uint32_t s, uint32_t h) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %3, -%4 op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixhi_f16 %0, %2, %3, -%4 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
+      : "=&v"(r)
+      : "v"(a0), "v"(a1), "v"(s), "v"(h));
+  return r;
+}
+// (hi, lo) fp16 operand pair of the products a[i] * s[i], i = 0..7.
+__device__ inline void split_products(const float* a, const half8& s, half8& hi, half8& lo) {
+  const uint4 su = __builtin_bit_cast(uint4, s);
+  uint4 h, l;
+  h.x = mul_to_f16x2(a[0], a[1], su.x);
+  h.y = mul_to_f16x2(a[2], a[3], su.y);
+  h.z = mul_to_f16x2(a[4], a[5], su.z);
+  h.w = mul_to_f16x2(a[6], a[7], su.w);
+  l.x = mul_residual_f16x2(a[0], a[1], su.x, h.x);
+  l.y = mul_residual_f16x2(a[2], a[3], su.y, h.y);
+  l.z = mul_residual_f16x2(a[4], a[5], su.z, h.z);
+  l.w = mul_residual_f16x2(a[6], a[7], su.w, h.w);
+  hi = __builtin_bit_cast(half8, h);
+  lo = __builtin_bit_cast(half8, l);
 }
 
 __device__ inline half8 load_half8(const uint8_t* p) {
@@ -155,7 +211,7 @@ __device__ void prepare_query(const DecodeArgs& a, int b, int h, float (*qf)[kD]
 
 // Partial of one query head: running max m (log2 domain), sum l, output o[128].
 __device__ inline float* partial_ptr(const DecodeArgs& a, int b, int hq, int split) {
-  return a.part + ((size_t(b) * a.Hq + hq) * size_t(a.nsplit + a.ntail) + split) * kPartialStride;
+  return a.part + ((size_t(b) * a.Hq + hq) * size_t(a.nsplit + 1) + split) * kPartialStride;
 }
 
 // Per-wave partials (m, l, o[128] per head) in shared memory; wave w's block starts
@@ -190,59 +246,73 @@ __device__ void merge_and_store(const DecodeArgs& a, int b, int h, int split, co
   }
 }
 
-// Attention over one 32-token chunk [t0, t0 + cnt) of the FP16 window of one
-// (kv-head, sequence); cnt may be 0. Scores: each wave takes 8 tokens, 8 lanes per
-// token each dotting 16 channels with every query head. Output: each thread
-// accumulates 2 channels over 8 tokens; the four token quarters are merged through
-// the per-wave partial slots of `wp` (all with the same max).
+// Attention over the FP16 window [Q, T) of one (kv-head, sequence) in 32-token
+// chunks with a running max. Scores: each wave takes 8 tokens of a chunk, 8 lanes
+// per token each dotting 16 channels with every query head. Output: each thread
+// accumulates 2 channels over 8 tokens of every chunk; the four token quarters are
+// left in the per-wave partial slots of `wp` (all with the same max).
 template <int HG>
-__device__ void tail_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt, float (*qf)[kD], const float* expo,
-                           float (*ts)[kG], const WaveParts& wp) {
-  __shared__ float m_s[HG], l_s[HG];
+__device__ void tail_window(const DecodeArgs& a, int b, int h, int Q, int T, float (*qf)[kD], const float* expo,
+                            float (*ts)[kG], const WaveParts& wp) {
+  __shared__ float m_s[HG], l_s[HG], alpha_s[HG];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const size_t bh = size_t(b) * a.Hkv + h;
-  {
-    const int tl = wave * 8 + lane / 8, cs = lane % 8;
-    float acc[HG];
-    for (int hh = 0; hh < HG; hh++) acc[hh] = 0.0f;
-    if (tl < cnt) {
-      const uint8_t* krow =
-          reinterpret_cast<const uint8_t*>(a.ringk + (bh * a.W + size_t((t0 + tl) % a.W)) * kD) + 32 * cs;
-      const half8 k0 = load_half8(krow), k1 = load_half8(krow + 16);
+  const int d2 = tid % 64, tq = tid / 64;
+  float o0[HG], o1[HG];
+  for (int hh = 0; hh < HG; hh++) o0[hh] = o1[hh] = 0.0f;
+  if (tid < HG) {
+    m_s[tid] = -INFINITY;
+    l_s[tid] = 0.0f;
+  }
+  __syncthreads();
+  for (int t0 = Q; t0 < T; t0 += kG) {
+    const int cnt = min(kG, T - t0);
+    {
+      const int tl = wave * 8 + lane / 8, cs = lane % 8;
+      float acc[HG];
+      for (int hh = 0; hh < HG; hh++) acc[hh] = 0.0f;
+      if (tl < cnt) {
+        const uint8_t* krow =
+            reinterpret_cast<const uint8_t*>(a.ringk + (bh * a.W + size_t((t0 + tl) % a.W)) * kD) + 32 * cs;
+        const half8 k0 = load_half8(krow), k1 = load_half8(krow + 16);
+        for (int hh = 0; hh < HG; hh++) {
+          float x = 0.0f;
+          for (int s = 0; s < 8; s++) x = __builtin_fmaf(qf[hh][16 * cs + s], float(k0[s]), x);
+          for (int s = 0; s < 8; s++) x = __builtin_fmaf(qf[hh][16 * cs + 8 + s], float(k1[s]), x);
+          acc[hh] = x;
+        }
+      }
       for (int hh = 0; hh < HG; hh++) {
-        float x = 0.0f;
-        for (int s = 0; s < 8; s++) x = __builtin_fmaf(qf[hh][16 * cs + s], float(k0[s]), x);
-        for (int s = 0; s < 8; s++) x = __builtin_fmaf(qf[hh][16 * cs + 8 + s], float(k1[s]), x);
-        acc[hh] = x;
+        float x = acc[hh];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        if (cs == 0) ts[hh][tl] = tl < cnt ? x * expo[hh] : -INFINITY;
       }
     }
+    __syncthreads();
+    for (int hh = wave; hh < HG; hh += kWaves) {
+      const float sc = lane < kG ? ts[hh][lane] : -INFINITY;
+      float m = sc;
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const float m_old = m_s[hh];
+      const float m_new = fmaxf(m_old, m);
+      const float p = lane < cnt ? exp2f(sc - m_new) : 0.0f;
+      float l = p;
+      for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+      if (lane < kG) ts[hh][lane] = p;
+      if (lane == 0) {
+        const float alpha = m_old == -INFINITY ? 0.0f : exp2f(m_old - m_new);
+        alpha_s[hh] = alpha;
+        l_s[hh] = l_s[hh] * alpha + l;
+        m_s[hh] = m_new;
+      }
+    }
+    __syncthreads();
     for (int hh = 0; hh < HG; hh++) {
-      float x = acc[hh];
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
-      x += __shfl_xor(x, 4);
-      if (cs == 0) ts[hh][tl] = tl < cnt ? x * expo[hh] : -INFINITY;
+      o0[hh] *= alpha_s[hh];
+      o1[hh] *= alpha_s[hh];
     }
-  }
-  __syncthreads();
-  for (int hh = wave; hh < HG; hh += kWaves) {
-    float sc = lane < kG ? ts[hh][lane] : -INFINITY;
-    float m = sc;
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    const float p = (lane < cnt && m != -INFINITY) ? exp2f(sc - m) : 0.0f;
-    float l = p;
-    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-    if (lane < kG) ts[hh][lane] = p;
-    if (lane == 0) {
-      m_s[hh] = m;
-      l_s[hh] = l;
-    }
-  }
-  __syncthreads();
-  {
-    const int d2 = tid % 64, tq = tid / 64;
-    float o0[HG], o1[HG];
-    for (int hh = 0; hh < HG; hh++) o0[hh] = o1[hh] = 0.0f;
     for (int j = 0; j < 8; j++) {
       const int tl = 8 * tq + j;
       if (tl < cnt) {
@@ -255,15 +325,16 @@ __device__ void tail_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt, f
         }
       }
     }
-    for (int hh = 0; hh < HG; hh++) {
-      wp.at(tq, hh, 2 + 2 * d2) = o0[hh];
-      wp.at(tq, hh, 3 + 2 * d2) = o1[hh];
-    }
-    if (tid < HG * kWaves) {
-      const int hh = tid % HG, w = tid / HG;
-      wp.at(w, hh, 0) = m_s[hh];
-      wp.at(w, hh, 1) = w == 0 ? l_s[hh] : 0.0f;
-    }
+    __syncthreads();
+  }
+  for (int hh = 0; hh < HG; hh++) {
+    wp.at(tq, hh, 2 + 2 * d2) = o0[hh];
+    wp.at(tq, hh, 3 + 2 * d2) = o1[hh];
+  }
+  if (tid < HG * kWaves) {
+    const int hh = tid % HG, w = tid / HG;
+    wp.at(w, hh, 0) = m_s[hh];
+    wp.at(w, hh, 1) = w == 0 ? l_s[hh] : 0.0f;
   }
 }
 
@@ -310,11 +381,15 @@ __device__ __forceinline__ void read_group(GroupRegs<BITS, NJ>& G, const uint8_t
 
 template <int BITS, int HG>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-  // MFMA columns: one per query head of the kv-head, replicated REP times over the
-  // 16 columns. The fp16 high and low parts of each B operand go through two MFMAs
-  // into the same accumulator.
-  constexpr int REP = 16 / HG;
-  constexpr int NJ = REP >= 4 ? 1 : 4 / REP;  // value channel groups handled per lane
+  // MFMA columns. Key side: U = 2 * HG column kinds, the fp16 high part of head u at
+  // u < HG and the low part of head U - 1 - u at u >= HG (u = column % U), repeated
+  // over the 16 columns; the two parts of a score are added across the paired
+  // columns. Value side: every column keeps its head and takes one of the channel
+  // groups j; the fp16 high and low parts of its B operand go through two MFMAs into
+  // the same accumulator.
+  constexpr int U = 2 * HG;
+  constexpr int NCOPY = 16 / HG;                // columns per head
+  constexpr int NJ = NCOPY >= 4 ? 1 : 4 / NCOPY;  // value channel groups handled per lane
   constexpr int GB = 2 * (kG * kD * BITS / 8) + 1024;
   constexpr int LPG = GB / 1024;              // 16-byte-per-lane loads per group block
   constexpr int NBUF = 3;                     // group blocks per wave in shared memory
@@ -327,20 +402,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ float expo[HG];
   __shared__ union {
     struct {
-      half8 hi[4][HG][4];  // key-side B operands per wave: [kc][head][k-block]
-      half8 lo[4][HG][4];
+      half8 b[4][U][4];  // key-side B operands per wave: [kc][column kind][k-block]
     } bk[kWaves];
     float ts[HG][kG];  // FP16-window scores / weights of one chunk
   } sh;
   static_assert(NBUF * GB >= HG * kPartialStride * 4, "wave partial must fit in the wave's ring");
   const WaveParts wp{reinterpret_cast<float*>(&ring[0][0]), NBUF * GB / 4};
 
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // 1-D grid: one FP16-window workgroup per (sequence, kv-head) first, then nsplit
+  // workgroups per (sequence, kv-head) over its quantized groups.
+  const int nwin = a.B * a.Hkv;
+  const bool tail = int(blockIdx.x) < nwin;
+  const int bh = tail ? int(blockIdx.x) : (int(blockIdx.x) - nwin) / a.nsplit;
+  const int split = tail ? a.nsplit : (int(blockIdx.x) - nwin) % a.nsplit;
+  const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const SeqDesc sd = a.seq[b];
   const int T = sd.t_old + sd.n_new, Q = sd.q_new;
   const int ng = Q / kG;
-  const bool tail = split >= a.nsplit;
 
   // This wave's groups.
   const int g0 = split * a.gps;
@@ -361,31 +440,62 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // Start streaming before the query preparation so that the two overlap.
   for (int r = 0; r < NBUF - 1 && r < n; r++) issue(r);
 
-  prepare_query<HG>(a, b, h, qf, expo);
+  // The FP16-window workgroup and rotated queries use the shared-memory query
+  // preparation; otherwise each wave prepares what its lanes need on its own.
+  if (tail || a.rotate) prepare_query<HG>(a, b, h, qf, expo);
 
   if (tail) {
-    const int t0 = Q + kG * (split - a.nsplit);
-    tail_chunk<HG>(a, b, h, t0, max(0, min(kG, T - t0)), qf, expo, sh.ts, wp);
+    tail_window<HG>(a, b, h, Q, T, qf, expo, sh.ts, wp);
     merge_and_store<HG>(a, b, h, split, wp);
     return;
   }
 
-  // MFMA lane roles: column n = lane % 16 (head n % HG, replica n / HG), k-block or
-  // row block kb = lane / 16.
+  // MFMA lane roles: column col = lane % 16, k-block or row block kb = lane / 16.
   const int col = lane % 16, kb = lane / 16;
-  const int hd = col % HG;
-  const int rho = col / HG;
-  const int jbase = (rho % (4 / NJ)) * NJ;
+  const int u = col % U;
+  const bool ishi = u < HG;
+  const int hd = ishi ? u : U - 1 - u;                  // query head of this column
+  const int kcopy = 2 * (col / U) + (ishi ? 0 : 1);     // which copy of the head (0..NCOPY-1)
+  const int jbase = (kcopy % (4 / NJ)) * NJ;            // first value channel group of the column
   // Key-side operand preparation: channel block cb = lane / 4 (8 channels) and head
   // (lane % 4) % HG + 4 * it. With this mapping the q . z_key sum of a head ends up
   // in exactly the lanes whose MFMA column belongs to that head.
   const int cb = lane / 4, hh0 = (lane % 4) % HG;
   const bool bwriter = (lane % 4) < HG;
 
+  // qreg: this lane's 8 channels of its heads, times softmax_scale * log2(e) and a
+  // power of two 2^-e per head that brings the head's largest entry below 1;
+  // ex = 2^e of the head of this lane's column.
   float qreg[ITEMS][8];
-  for (int it = 0; it < ITEMS; it++)
-    for (int s = 0; s < 8; s++) qreg[it][s] = qf[hh0 + 4 * it][8 * cb + s];
-  const float ex = expo[hd];
+  float ex;
+  if (a.rotate) {
+    for (int it = 0; it < ITEMS; it++)
+      for (int s = 0; s < 8; s++) qreg[it][s] = qf[hh0 + 4 * it][8 * cb + s];
+    ex = expo[hd];
+  } else {
+    float exo[ITEMS];
+    for (int it = 0; it < ITEMS; it++) {
+      const half8 qh = load_half8(reinterpret_cast<const uint8_t*>(
+          a.q + (size_t(b) * a.Hq + h * HG + hh0 + 4 * it) * kD + 8 * cb));
+      float m = 0.0f;
+      for (int s = 0; s < 8; s++) {
+        qreg[it][s] = float(qh[s]) * a.scale_log2;
+        m = fmaxf(m, fabsf(qreg[it][s]));
+      }
+      m = wave_max_rows(row_max_stride4(m));
+      int e = 0;
+      if (m > 0.0f) frexpf(m, &e);
+      for (int s = 0; s < 8; s++) qreg[it][s] = ldexpf(qreg[it][s], -e);
+      exo[it] = ldexpf(1.0f, e);
+    }
+    // High-part columns own their head's exponent (lane % 4 matches); low-part
+    // columns take it from the paired column.
+    float exh;
+    if constexpr (ITEMS == 1) exh = exo[0];
+    else exh = hd >= 4 ? exo[1] : exo[0];
+    const float exp_ = partner<U>(exh);
+    ex = ishi ? exh : exp_;
+  }
 
   float4v oacc[8];
   for (int t = 0; t < 8; t++) oacc[t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -406,17 +516,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int it = 0; it < ITEMS; it++) {
       const int hh = hh0 + 4 * it;
       half8 hi, lo;
+      split_products(qreg[it], g.ks, hi, lo);
       float z = 0.0f;
-      for (int s = 0; s < 8; s++) {
-        const _Float16 hv = _Float16(qreg[it][s] * float(g.ks[s]));
-        hi[s] = hv;
-        lo[s] = _Float16(__builtin_fmaf(qreg[it][s], float(g.ks[s]), -float(hv)));
-        z = __builtin_fmaf(qreg[it][s], float(g.kz[s]), z);
-      }
+      for (int s = 0; s < 8; s++) z = __builtin_fmaf(qreg[it][s], float(g.kz[s]), z);
       qz[it] = wave_sum_rows(row_sum_stride4(z));
       if (bwriter) {
-        sh.bk[wave].hi[cb / 4][hh][cb % 4] = hi;
-        sh.bk[wave].lo[cb / 4][hh][cb % 4] = lo;
+        sh.bk[wave].b[cb / 4][hh][cb % 4] = hi;
+        sh.bk[wave].b[cb / 4][U - 1 - hh][cb % 4] = lo;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -425,18 +531,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     float qzc;
     if constexpr (ITEMS == 1) qzc = qz[0];
     else qzc = hd >= 4 ? qz[1] : qz[0];
+    if (!ishi) qzc = 0.0f;  // q . z_key enters once, through the high-part column
     // Scores of the group's 32 tokens: rows 4*kb + i of token tiles 0 and 1.
     r0 = float4v{qzc, qzc, qzc, qzc};
     r1 = r0;
     for (int kc = 0; kc < 4; kc++) {
-      const half8 bh = sh.bk[wave].hi[kc][hd][kb];
-      const half8 bl = sh.bk[wave].lo[kc][hd][kb];
-      const half8 a0 = code_operand<BITS>(g.kc0, g.kc1, 2 * kc);
-      const half8 a1 = code_operand<BITS>(g.kc0, g.kc1, 2 * kc + 1);
-      r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bh, r0, 0, 0, 0);
-      r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bh, r1, 0, 0, 0);
-      r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bl, r0, 0, 0, 0);
-      r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bl, r1, 0, 0, 0);
+      const half8 bk = sh.bk[wave].b[kc][u][kb];
+      r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(g.kc0, g.kc1, 2 * kc), bk, r0, 0, 0, 0);
+      r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(g.kc0, g.kc1, 2 * kc + 1), bk, r1, 0, 0, 0);
+    }
+    for (int i = 0; i < 4; i++) {
+      r0[i] += partner<U>(r0[i]);
+      r1[i] += partner<U>(r1[i]);
     }
   };
 
@@ -444,11 +550,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const float sc[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
     // Online softmax. Scores stay in the prescaled units S (log2 units are ex * S);
     // the running max m_run is kept in the same units.
+    // The cross-lane max is only formed when some score exceeds the running max.
     float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                        fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mloc = wave_max_rows(mloc);
-    const float m_new = fmaxf(m_run, mloc);
-    if (__ballot(m_new > m_run)) {
+    if (__ballot(mloc > m_run)) {
+      const float m_new = fmaxf(m_run, wave_max_rows(mloc));
       const float alpha = m_run == -INFINITY ? 0.0f : exp2f(ex * (m_run - m_new));
       for (int t = 0; t < 8; t++) oacc[t] *= alpha;
       l_run *= alpha;
@@ -464,13 +570,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     // Value side: B = p * s_value (fp16 high + low parts), plus sum p * z_value.
     half8 bvh[NJ], bvl[NJ];
     for (int jr = 0; jr < NJ; jr++) {
+      split_products(p, g.vs[jr], bvh[jr], bvl[jr]);
       float z = zacc[jr];
-      for (int s = 0; s < 8; s++) {
-        const _Float16 hv = _Float16(p[s] * float(g.vs[jr][s]));
-        bvh[jr][s] = hv;
-        bvl[jr][s] = _Float16(__builtin_fmaf(p[s], float(g.vs[jr][s]), -float(hv)));
-        z = __builtin_fmaf(p[s], float(g.vz[jr][s]), z);
-      }
+      for (int s = 0; s < 8; s++) z = __builtin_fmaf(p[s], float(g.vz[jr][s]), z);
       zacc[jr] = z;
     }
     for (int t = 0; t < 8; t++) {
@@ -506,12 +608,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   for (int jr = 0; jr < NJ; jr++) zs[jr] = wave_sum_rows(zacc[jr]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  if (kb == 0 && rho == 0) {
+  if (kb == 0 && kcopy == 0) {
     wp.at(wave, hd, 0) = m_run == -INFINITY ? -INFINITY : ex * m_run;
     wp.at(wave, hd, 1) = l_tot;
   }
   for (int t = 0; t < 8; t++) {
-    if (rho == (t / 2) / NJ)
+    if (kcopy == (t / 2) / NJ)
       for (int i = 0; i < 4; i++) wp.at(wave, hd, 2 + 16 * t + 4 * kb + i) = oacc[t][i] + zs[(t / 2) % NJ];
   }
   merge_and_store<HG>(a, b, h, split, wp);
@@ -523,7 +625,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // slices of 16 threads sum strided subsets of the partials.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineChannels = 16;
-constexpr int kCombineMaxParts = kMaxSplits + kMaxResidual / kGroup + 1;
+constexpr int kCombineMaxParts = kMaxSplits + 1;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part,
                                                                   float* __restrict__ out, int Hq, int nparts) {
@@ -573,12 +675,31 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
 }
 
 template <int BITS, int HG>
+int resident_blocks_of() {
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<BITS, HG>, 256, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return per_cu * cus;
+}
+
+template <int BITS, int HG>
 hipError_t launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<BITS, HG>), dim3(a.nsplit + a.ntail, a.Hkv, B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<BITS, HG>), dim3((a.nsplit + 1) * a.Hkv * B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+int decode_resident_blocks(int bits, int hg) {
+  if (bits == 2) return hg == 1 ? resident_blocks_of<2, 1>() : hg == 2 ? resident_blocks_of<2, 2>()
+                      : hg == 4 ? resident_blocks_of<2, 4>() : resident_blocks_of<2, 8>();
+  return hg == 1 ? resident_blocks_of<4, 1>() : hg == 2 ? resident_blocks_of<4, 2>()
+         : hg == 4 ? resident_blocks_of<4, 4>() : resident_blocks_of<4, 8>();
+}
 
 hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* q, float* out,
                          int32_t groups_per_split, int32_t nsplit, float scale_log2, int rotate, hipStream_t stream,
@@ -596,7 +717,7 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   a.W = L.W;
   a.gps = groups_per_split;
   a.nsplit = nsplit;
-  a.ntail = L.R / kG + 1;
+  a.B = L.B;
   a.rotate = rotate;
   a.scale_log2 = scale_log2;
   const int hg = L.Hq / L.Hkv;
@@ -615,7 +736,7 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   }
   if (e != hipSuccess) return e;
   if (prof_stop && hipEventRecord(prof_stop, stream) != hipSuccess) return hipGetLastError();
-  hipLaunchKernelGGL(combine_kernel, dim3(L.Hq, L.B, kD / kCombineChannels), dim3(kCombineThreads), 0, stream, a.part, out, L.Hq, a.nsplit + a.ntail);
+  hipLaunchKernelGGL(combine_kernel, dim3(L.Hq, L.B, kD / kCombineChannels), dim3(kCombineThreads), 0, stream, a.part, out, L.Hq, a.nsplit + 1);
   return hipGetLastError();
 }
 

@@ -94,7 +94,7 @@ Layout make_layout(const kvq_config* cfg) {
   L.ringv_off = off;
   off = align256(off + ring);
   L.part_off = off;
-  off = align256(off + size_t(L.B) * L.Hq * size_t(L.max_splits + L.R / kvq::kGroup + 1) * kvq::kPartialStride * 4);
+  off = align256(off + size_t(L.B) * L.Hq * size_t(L.max_splits + 1) * kvq::kPartialStride * 4);
   L.total = off;
   return L;
 }
@@ -113,6 +113,7 @@ struct kvq_cache {
   std::vector<int64_t> T, Q;
   int32_t groups_per_split = 0;
   hipEvent_t prof_start = nullptr, prof_stop = nullptr;
+  int resident_blocks = 0;
   SeqDesc* staging[kStaging] = {};
   hipEvent_t staging_done[kStaging] = {};
   int next_staging = 0;
@@ -248,11 +249,19 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, const int32_t*
   if (!k || !v) return fail(KVQ_ERR_INVALID_ARG, "k and v must be device pointers when tokens are appended");
 
   // Host bookkeeping: new lengths, groups leaving the window, tokens entering it.
-  int slot = c->next_staging;
-  c->next_staging = (slot + 1) % kStaging;
-  if (hipEventSynchronize(c->staging_done[slot]) != hipSuccess)
-    return fail(KVQ_ERR_HIP, "waiting for a staging buffer failed: %s", hipGetErrorString(hipGetLastError()));
-  SeqDesc* d = c->staging[slot];
+  // Small batches pass the per-sequence records to the kernels by value; larger ones
+  // upload them from a pinned staging buffer.
+  const bool inl = B <= kvq::kInlineSeqs;
+  kvq::SeqArgs sa;
+  SeqDesc* d = sa.inl;
+  int slot = -1;
+  if (!inl) {
+    slot = c->next_staging;
+    c->next_staging = (slot + 1) % kStaging;
+    if (hipEventSynchronize(c->staging_done[slot]) != hipSuccess)
+      return fail(KVQ_ERR_HIP, "waiting for a staging buffer failed: %s", hipGetErrorString(hipGetLastError()));
+    d = c->staging[slot];
+  }
   int32_t max_flush = 0, max_ring = 0;
   std::vector<int64_t> T2(B), Q2(B);
   for (int b = 0; b < B; b++) {
@@ -269,14 +278,18 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, const int32_t*
     max_ring = std::max<int32_t>(max_ring, int32_t(std::max<int64_t>(0, T2[b] - first_kept)));
   }
   SeqDesc* dev_seq = reinterpret_cast<SeqDesc*>(c->base + c->L.seq_off);
-  if (hipMemcpyAsync(dev_seq, d, sizeof(SeqDesc) * B, hipMemcpyHostToDevice, stream) != hipSuccess ||
-      hipEventRecord(c->staging_done[slot], stream) != hipSuccess)
+  sa.dev = dev_seq;
+  sa.state = dev_seq;
+  sa.inl_valid = inl ? 1 : 0;
+  if (!inl && (hipMemcpyAsync(dev_seq, d, sizeof(SeqDesc) * B, hipMemcpyHostToDevice, stream) != hipSuccess ||
+               hipEventRecord(c->staging_done[slot], stream) != hipSuccess))
     return fail(KVQ_ERR_HIP, "uploading sequence state failed: %s", hipGetErrorString(hipGetLastError()));
   hipError_t e = hipSuccess;
   if (max_flush > 0)
-    e = kvq::launch_flush(c->L, c->base, dev_seq, k, v, n_max, max_flush, c->cfg.rotate, stream);
-  if (e == hipSuccess && max_ring > 0)
-    e = kvq::launch_ring_write(c->L, c->base, dev_seq, k, v, n_max, max_ring, c->cfg.rotate, stream);
+    e = kvq::launch_flush(c->L, c->base, sa, k, v, n_max, max_flush, c->cfg.rotate, stream);
+  // The window-write kernel always runs: with inline records it also stores them.
+  if (e == hipSuccess && (max_ring > 0 || inl))
+    e = kvq::launch_ring_write(c->L, c->base, sa, k, v, n_max, std::max(max_ring, 1), c->cfg.rotate, stream);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append kernels failed: %s", hipGetErrorString(e));
   c->T = T2;
   c->Q = Q2;
@@ -292,12 +305,18 @@ kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, hipStre
     max_groups = std::max(max_groups, c->Q[b] / kvq::kGroup);
   }
   int64_t gps = c->groups_per_split;
-  if (gps == 0) {
-    // Aim for about 2048 workgroups over the whole batch (8 per CU on 256 CUs)
-    // while giving each of the 4 waves of a workgroup a few groups to stream.
-    int64_t work = max_groups * c->cfg.batch * c->cfg.num_kv_heads;
-    gps = std::max<int64_t>(16, (work + 2047) / 2048);
+  if (gps == 0 && max_groups > 0) {
+    // One round of workgroups: as many splits per (sequence, kv-head) as fit on the
+    // device at once next to the FP16-window workgroups.
+    if (c->resident_blocks == 0)
+      c->resident_blocks = std::max(1, kvq::decode_resident_blocks(c->cfg.bits,
+                                                                   c->cfg.num_q_heads / c->cfg.num_kv_heads));
+    const int64_t bh = int64_t(c->cfg.batch) * c->cfg.num_kv_heads;
+    const int64_t slots = std::max<int64_t>(bh, c->resident_blocks - std::min<int64_t>(bh, c->resident_blocks / 4));
+    const int64_t splits = std::max<int64_t>(1, slots / bh);
+    gps = std::max<int64_t>(kvq::kMinGroupsPerSplit, (max_groups + splits - 1) / splits);
   }
+  if (gps == 0) gps = kvq::kMinGroupsPerSplit;
   int64_t nsplit = max_groups == 0 ? 0 : (max_groups + gps - 1) / gps;
   if (nsplit > c->L.max_splits) {
     gps = (max_groups + c->L.max_splits - 1) / c->L.max_splits;

@@ -22,6 +22,18 @@ struct SeqDesc {
   int32_t q_new;
 };
 
+// Per-sequence records of one append, passed to its kernels by value when the batch
+// is small (no host-to-device copy), otherwise read from the device array `dev`.
+// With `inl_valid`, the window-write kernel also stores them to `state`, the array
+// the decode kernel reads.
+constexpr int kInlineSeqs = 64;
+struct SeqArgs {
+  SeqDesc inl[kInlineSeqs];
+  const SeqDesc* dev;
+  SeqDesc* state;
+  int inl_valid;
+};
+
 struct Layout {
   int32_t B, Hq, Hkv, bits, R, W;  // W = R + G ring slots
   int64_t gcap;                     // group blocks per (b, h)
@@ -31,12 +43,14 @@ struct Layout {
 };
 
 // Launchers (return hipGetLastError() of the launch).
-hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* k,
+hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqArgs& seq, const void* k,
                         const void* v, int32_t n_max, int32_t max_flush_groups, int rotate,
                         hipStream_t stream);
-hipError_t launch_ring_write(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* k,
+hipError_t launch_ring_write(const Layout& L, uint8_t* base, const SeqArgs& seq, const void* k,
                              const void* v, int32_t n_max, int32_t max_ring_tokens, int rotate,
                              hipStream_t stream);
+// Workgroups of the decode split kernel that fit on the current device at once.
+int decode_resident_blocks(int bits, int hg);
 hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* q,
                          float* out, int32_t groups_per_split, int32_t nsplit, float scale_log2,
                          int rotate, hipStream_t stream, hipEvent_t prof_start, hipEvent_t prof_stop);
