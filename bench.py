@@ -137,7 +137,69 @@ def cpu_baseline(w, heads=4, steps=3):
                       f"{dt:.1f} s timed, numpy with one BLAS thread"}
 
 
+COPY_BYTES = 1 << 30
+KERNEL_SOURCE = os.path.join(ROOT, "bit_asymmetric_kv_amd", "csrc", "decode.hip")
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of COPY_BYTES bytes, repeated 5 times: run under
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to learn how those counters scale."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 5}))
+
+
+def _counter_per_dispatch(path, kernel_substr, counter):
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} samples for kernels matching {kernel_substr!r} under {path}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def summarize_traffic(dec_fetch, dec_write, copy_fetch, copy_write, workload, out_path):
+    """HBM bytes per decode split launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+    each scaled by the same counter's reading for the calibration copy."""
+    f_dec, n1 = _counter_per_dispatch(dec_fetch, "decode_split_kernel", "FETCH_SIZE")
+    w_dec, n2 = _counter_per_dispatch(dec_write, "decode_split_kernel", "WRITE_SIZE")
+    f_cp, _ = _counter_per_dispatch(copy_fetch, "copy", "FETCH_SIZE")
+    w_cp, _ = _counter_per_dispatch(copy_write, "copy", "WRITE_SIZE")
+    f_scale = COPY_BYTES / (f_cp * 1024.0)
+    w_scale = COPY_BYTES / (w_cp * 1024.0)
+    res = {"workload": workload,
+           "bytes_per_launch": int(f_dec * 1024 * f_scale + w_dec * 1024 * w_scale),
+           "fetch_kib_per_dispatch": f_dec, "write_kib_per_dispatch": w_dec,
+           "copy_fetch_kib": f_cp, "copy_write_kib": w_cp, "copy_bytes": COPY_BYTES,
+           "fetch_scale": f_scale, "write_scale": w_scale, "dispatches": [n1, n2],
+           "kernel_source_sha256": kernel_source_hash()}
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--calibrate-copy":
+        calibrate_copy()
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-traffic":
+        summarize_traffic(*sys.argv[2:8])
+        return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -230,7 +292,8 @@ def main():
         try:
             with open(args.traffic_json) as f:
                 t = json.load(f)
-            if t.get("workload") == w.name:
+            # counters taken on another build of the kernel no longer describe it
+            if t.get("workload") == w.name and t.get("kernel_source_sha256") == kernel_source_hash():
                 traffic = t.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
