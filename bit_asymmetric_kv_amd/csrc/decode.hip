@@ -46,7 +46,9 @@ struct DecodeArgs {
   const __half* q;
   float* part;
   long long gcap;
-  int B, Hkv, Hq, W, gps, nsplit, rotate;  // partials per query head: nsplit + 1 (FP16 window last)
+  int B, Hkv, Hq, W, gps, nsplit, rotate;
+  int wblocks;  // FP16-window workgroups per (sequence, kv-head); partials per query
+                // head: nsplit (quantized groups) + wblocks (FP16 window)
   float scale_log2;
 };
 
@@ -129,40 +131,26 @@ __device__ inline float row_sum_stride4(float x) {
   return x;
 }
 
-// Two fp16 products rounded once from fp32 operands and an fp16 pair:
-// r.lo = f16(a0 * s.lo), r.hi = f16(a1 * s.hi)  (v_fma_mixlo / v_fma_mixhi).
-__device__ inline uint32_t mul_to_f16x2(float a0, float a1, uint32_t s) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, %1, %3, 0 op_sel_hi:[0,1,0]\n\t"
-      "v_fma_mixhi_f16 %0, %2, %3, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
-      : "=&v"(r)
-      : "v"(a0), "v"(a1), "v"(s));
-  return r;
+// (hi, lo) fp16 operand pair of the products x_i = a[i] * s[i], i = 0..7, with
+// hi + lo = x to about 21 bits: hi = fp16(ah[i] * s[i]) with ah = fp16(a) (packed
+// fp16 multiply), lo = fp16(a[i] * s[i] - hi[i]) with the residual formed by one
+// fused fp32 operation. Mixed-precision fused forms that round straight to fp16
+// are several times slower on this hardware than these.
+__device__ inline void split_products(const float* a, const half8& ah, const half8& s, half8& hi, half8& lo) {
+  hi = ah * s;
+  for (int i = 0; i < 8; i += 2) {
+    float l0 = __builtin_fmaf(a[i], float(s[i]), -float(hi[i]));
+    float l1 = __builtin_fmaf(a[i + 1], float(s[i + 1]), -float(hi[i + 1]));
+    asm("" : "+v"(l0), "+v"(l1));
+    lo[i] = _Float16(l0);
+    lo[i + 1] = _Float16(l1);
+  }
 }
-// The low parts of the same products: r.lo = f16(a0 * s.lo - h.lo),
-// r.hi = f16(a1 * s.hi - h.hi), each fused and rounded once.
-__device__ inline uint32_t mul_residual_f16x2(float a0, float a1, uint32_t s, uint32_t h) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, %1, %3, -%4 op_sel_hi:[0,1,1]\n\t"
-      "v_fma_mixhi_f16 %0, %2, %3, -%4 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
-      : "=&v"(r)
-      : "v"(a0), "v"(a1), "v"(s), "v"(h));
+
+__device__ inline half8 to_half8(const float* a) {
+  half8 r;
+  for (int i = 0; i < 8; i++) r[i] = _Float16(a[i]);
   return r;
-}
-// (hi, lo) fp16 operand pair of the products a[i] * s[i], i = 0..7.
-__device__ inline void split_products(const float* a, const half8& s, half8& hi, half8& lo) {
-  const uint4 su = __builtin_bit_cast(uint4, s);
-  uint4 h, l;
-  h.x = mul_to_f16x2(a[0], a[1], su.x);
-  h.y = mul_to_f16x2(a[2], a[3], su.y);
-  h.z = mul_to_f16x2(a[4], a[5], su.z);
-  h.w = mul_to_f16x2(a[6], a[7], su.w);
-  l.x = mul_residual_f16x2(a[0], a[1], su.x, h.x);
-  l.y = mul_residual_f16x2(a[2], a[3], su.y, h.y);
-  l.z = mul_residual_f16x2(a[4], a[5], su.z, h.z);
-  l.w = mul_residual_f16x2(a[6], a[7], su.w, h.w);
-  hi = __builtin_bit_cast(half8, h);
-  lo = __builtin_bit_cast(half8, l);
 }
 
 __device__ inline half8 load_half8(const uint8_t* p) {
@@ -211,7 +199,7 @@ __device__ void prepare_query(const DecodeArgs& a, int b, int h, float (*qf)[kD]
 
 // Partial of one query head: running max m (log2 domain), sum l, output o[128].
 __device__ inline float* partial_ptr(const DecodeArgs& a, int b, int hq, int split) {
-  return a.part + ((size_t(b) * a.Hq + hq) * size_t(a.nsplit + 1) + split) * kPartialStride;
+  return a.part + ((size_t(b) * a.Hq + hq) * size_t(a.nsplit + a.wblocks) + split) * kPartialStride;
 }
 
 // Per-wave partials (m, l, o[128] per head) in shared memory; wave w's block starts
@@ -246,95 +234,76 @@ __device__ void merge_and_store(const DecodeArgs& a, int b, int h, int split, co
   }
 }
 
-// Attention over the FP16 window [Q, T) of one (kv-head, sequence) in 32-token
-// chunks with a running max. Scores: each wave takes 8 tokens of a chunk, 8 lanes
-// per token each dotting 16 channels with every query head. Output: each thread
-// accumulates 2 channels over 8 tokens of every chunk; the four token quarters are
-// left in the per-wave partial slots of `wp` (all with the same max).
+// Attention of the HG query heads over one chunk of at most 32 tokens of the FP16
+// window, tokens [t0, t0 + cnt), computed by one wave; the wave's partial (m, l, o)
+// goes to its slot of `wp`. All loads of the chunk are issued first. Scores: lane l
+// takes token l % 32 and channel half l / 32. Weighted values: lane l accumulates
+// channels 2l and 2l + 1 over the chunk's tokens.
 template <int HG>
-__device__ void tail_window(const DecodeArgs& a, int b, int h, int Q, int T, float (*qf)[kD], const float* expo,
-                            float (*ts)[kG], const WaveParts& wp) {
-  __shared__ float m_s[HG], l_s[HG], alpha_s[HG];
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const size_t bh = size_t(b) * a.Hkv + h;
-  const int d2 = tid % 64, tq = tid / 64;
+__device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt, const float (*qf)[kD],
+                             const float* expo, const WaveParts& wp, int wave, int lane) {
+  if (cnt <= 0) {
+    if (lane < HG) {
+      wp.at(wave, lane, 0) = -INFINITY;
+      wp.at(wave, lane, 1) = 0.0f;
+    }
+    return;
+  }
+  const size_t row0 = (size_t(b) * a.Hkv + h) * size_t(a.W);
+  const int s0 = t0 % a.W;
+  const int tl = lane % 32, hf = lane / 32;
+  const bool kval = tl < cnt;
+  uint4 kr[8];
+  {
+    int slot = s0 + (kval ? tl : 0);
+    if (slot >= a.W) slot -= a.W;
+    const uint4* krow = reinterpret_cast<const uint4*>(a.ringk + (row0 + slot) * kD + 64 * hf);
+    for (int i = 0; i < 8; i++) kr[i] = krow[i];
+  }
+  uint32_t vr[kG];
+  for (int t = 0; t < kG; t++) {
+    int slot = s0 + (t < cnt ? t : 0);
+    if (slot >= a.W) slot -= a.W;
+    vr[t] = *reinterpret_cast<const uint32_t*>(a.ringv + (row0 + slot) * kD + 2 * lane);
+  }
+
+  float kf[64];
+  for (int i = 0; i < 8; i++) {
+    const half8 k8 = __builtin_bit_cast(half8, kr[i]);
+    for (int e = 0; e < 8; e++) kf[8 * i + e] = float(k8[e]);
+  }
+  float p[HG];
+  for (int hh = 0; hh < HG; hh++) {
+    float x = 0.0f;
+    for (int d = 0; d < 64; d++) x = __builtin_fmaf(qf[hh][64 * hf + d], kf[d], x);
+    x += __shfl_xor(x, 32);
+    const float sc = kval ? x * expo[hh] : -INFINITY;
+    float m = sc;
+    for (int off = 16; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    p[hh] = kval ? exp2f(sc - m) : 0.0f;
+    float l = p[hh];
+    for (int off = 16; off > 0; off >>= 1) l += __shfl_xor(l, off);
+    if (lane == 0) {
+      wp.at(wave, hh, 0) = m;
+      wp.at(wave, hh, 1) = l;
+    }
+  }
   float o0[HG], o1[HG];
   for (int hh = 0; hh < HG; hh++) o0[hh] = o1[hh] = 0.0f;
-  if (tid < HG) {
-    m_s[tid] = -INFINITY;
-    l_s[tid] = 0.0f;
-  }
-  __syncthreads();
-  for (int t0 = Q; t0 < T; t0 += kG) {
-    const int cnt = min(kG, T - t0);
-    {
-      const int tl = wave * 8 + lane / 8, cs = lane % 8;
-      float acc[HG];
-      for (int hh = 0; hh < HG; hh++) acc[hh] = 0.0f;
-      if (tl < cnt) {
-        const uint8_t* krow =
-            reinterpret_cast<const uint8_t*>(a.ringk + (bh * a.W + size_t((t0 + tl) % a.W)) * kD) + 32 * cs;
-        const half8 k0 = load_half8(krow), k1 = load_half8(krow + 16);
-        for (int hh = 0; hh < HG; hh++) {
-          float x = 0.0f;
-          for (int s = 0; s < 8; s++) x = __builtin_fmaf(qf[hh][16 * cs + s], float(k0[s]), x);
-          for (int s = 0; s < 8; s++) x = __builtin_fmaf(qf[hh][16 * cs + 8 + s], float(k1[s]), x);
-          acc[hh] = x;
-        }
-      }
+  for (int t = 0; t < kG; t++) {
+    if (t < cnt) {
+      const half2v vv = __builtin_bit_cast(half2v, vr[t]);
+      const float v0 = float(vv[0]), v1 = float(vv[1]);
       for (int hh = 0; hh < HG; hh++) {
-        float x = acc[hh];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        if (cs == 0) ts[hh][tl] = tl < cnt ? x * expo[hh] : -INFINITY;
+        const float pt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[hh]), t));
+        o0[hh] = __builtin_fmaf(pt, v0, o0[hh]);
+        o1[hh] = __builtin_fmaf(pt, v1, o1[hh]);
       }
     }
-    __syncthreads();
-    for (int hh = wave; hh < HG; hh += kWaves) {
-      const float sc = lane < kG ? ts[hh][lane] : -INFINITY;
-      float m = sc;
-      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      const float m_old = m_s[hh];
-      const float m_new = fmaxf(m_old, m);
-      const float p = lane < cnt ? exp2f(sc - m_new) : 0.0f;
-      float l = p;
-      for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-      if (lane < kG) ts[hh][lane] = p;
-      if (lane == 0) {
-        const float alpha = m_old == -INFINITY ? 0.0f : exp2f(m_old - m_new);
-        alpha_s[hh] = alpha;
-        l_s[hh] = l_s[hh] * alpha + l;
-        m_s[hh] = m_new;
-      }
-    }
-    __syncthreads();
-    for (int hh = 0; hh < HG; hh++) {
-      o0[hh] *= alpha_s[hh];
-      o1[hh] *= alpha_s[hh];
-    }
-    for (int j = 0; j < 8; j++) {
-      const int tl = 8 * tq + j;
-      if (tl < cnt) {
-        const __half2 vv =
-            *reinterpret_cast<const __half2*>(a.ringv + (bh * a.W + size_t((t0 + tl) % a.W)) * kD + 2 * d2);
-        const float v0 = __low2float(vv), v1 = __high2float(vv);
-        for (int hh = 0; hh < HG; hh++) {
-          o0[hh] = __builtin_fmaf(ts[hh][tl], v0, o0[hh]);
-          o1[hh] = __builtin_fmaf(ts[hh][tl], v1, o1[hh]);
-        }
-      }
-    }
-    __syncthreads();
   }
   for (int hh = 0; hh < HG; hh++) {
-    wp.at(tq, hh, 2 + 2 * d2) = o0[hh];
-    wp.at(tq, hh, 3 + 2 * d2) = o1[hh];
-  }
-  if (tid < HG * kWaves) {
-    const int hh = tid % HG, w = tid / HG;
-    wp.at(w, hh, 0) = m_s[hh];
-    wp.at(w, hh, 1) = w == 0 ? l_s[hh] : 0.0f;
+    wp.at(wave, hh, 2 + 2 * lane) = o0[hh];
+    wp.at(wave, hh, 3 + 2 * lane) = o1[hh];
   }
 }
 
@@ -361,21 +330,99 @@ struct GroupRegs {
   half8 vs[NJ], vz[NJ];      // value scale / zero of this lane's 8 tokens per channel group
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
+
+// Byte offset of a shared-memory object inside the workgroup's LDS allocation.
+__device__ inline uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cu8*)p));
+}
+
+// The reads of a group block are written as one asm block that also waits for
+// them. The block's bytes arrive through direct HBM->LDS loads whose completion the
+// loop tracks itself with vmcnt (at most one later group still in flight); a
+// compiler-generated LDS read of the same array would instead be preceded by a wait
+// for every outstanding direct load, which drains the prefetch ring at every group.
+// Addresses: a0 = block + 16 * lane (code words), a1 = block + 16 * cb (key scale /
+// zero), a2 = block + 16 * (4 * kb + jbase) (value scale / zero).
 template <int BITS, int NJ>
 __device__ __forceinline__ void read_group(GroupRegs<BITS, NJ>& G, const uint8_t* blk, int lane, int cb, int kb,
                                            int jbase) {
-  constexpr int CB = kG * kD * BITS / 8;
-  G.kc0 = *reinterpret_cast<const uint4*>(blk + 16 * lane);
-  G.vc0 = *reinterpret_cast<const uint4*>(blk + CB + 16 * lane);
-  if constexpr (BITS == 4) {
-    G.kc1 = *reinterpret_cast<const uint4*>(blk + 1024 + 16 * lane);
-    G.vc1 = *reinterpret_cast<const uint4*>(blk + CB + 1024 + 16 * lane);
+  const uint32_t base = lds_offset(blk);
+  const uint32_t a0 = base + 16 * lane, a1 = base + 16 * cb, a2 = base + 16 * (kb * 4 + jbase);
+  u32x4 kc0, kc1, vc0, vc1, ks, kz, vs0, vz0, vs1, vz1;
+  if constexpr (BITS == 2 && NJ == 1) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:1024\n\t"
+        "ds_read_b128 %2, %7 offset:2048\n\t"
+        "ds_read_b128 %3, %7 offset:2304\n\t"
+        "ds_read_b128 %4, %8 offset:2560\n\t"
+        "ds_read_b128 %5, %8 offset:2816\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kc0), "=&v"(vc0), "=&v"(ks), "=&v"(kz), "=&v"(vs0), "=&v"(vz0)
+        : "v"(a0), "v"(a1), "v"(a2)
+        : "memory");
+  } else if constexpr (BITS == 2 && NJ == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %9 offset:2048\n\t"
+        "ds_read_b128 %3, %9 offset:2304\n\t"
+        "ds_read_b128 %4, %10 offset:2560\n\t"
+        "ds_read_b128 %5, %10 offset:2816\n\t"
+        "ds_read_b128 %6, %10 offset:2576\n\t"
+        "ds_read_b128 %7, %10 offset:2832\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kc0), "=&v"(vc0), "=&v"(ks), "=&v"(kz), "=&v"(vs0), "=&v"(vz0), "=&v"(vs1), "=&v"(vz1)
+        : "v"(a0), "v"(a1), "v"(a2)
+        : "memory");
+  } else if constexpr (BITS == 4 && NJ == 1) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %9 offset:4096\n\t"
+        "ds_read_b128 %5, %9 offset:4352\n\t"
+        "ds_read_b128 %6, %10 offset:4608\n\t"
+        "ds_read_b128 %7, %10 offset:4864\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kc0), "=&v"(kc1), "=&v"(vc0), "=&v"(vc1), "=&v"(ks), "=&v"(kz), "=&v"(vs0), "=&v"(vz0)
+        : "v"(a0), "v"(a1), "v"(a2)
+        : "memory");
+  } else {
+    static_assert(BITS == 4 && NJ == 2, "group block read: unsupported configuration");
+    asm volatile(
+        "ds_read_b128 %0, %10\n\t"
+        "ds_read_b128 %1, %10 offset:1024\n\t"
+        "ds_read_b128 %2, %10 offset:2048\n\t"
+        "ds_read_b128 %3, %10 offset:3072\n\t"
+        "ds_read_b128 %4, %11 offset:4096\n\t"
+        "ds_read_b128 %5, %11 offset:4352\n\t"
+        "ds_read_b128 %6, %12 offset:4608\n\t"
+        "ds_read_b128 %7, %12 offset:4864\n\t"
+        "ds_read_b128 %8, %12 offset:4624\n\t"
+        "ds_read_b128 %9, %12 offset:4880\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kc0), "=&v"(kc1), "=&v"(vc0), "=&v"(vc1), "=&v"(ks), "=&v"(kz), "=&v"(vs0), "=&v"(vz0),
+          "=&v"(vs1), "=&v"(vz1)
+        : "v"(a0), "v"(a1), "v"(a2)
+        : "memory");
   }
-  G.ks = load_half8(blk + 2 * CB + 16 * cb);
-  G.kz = load_half8(blk + 2 * CB + 256 + 16 * cb);
-  for (int jr = 0; jr < NJ; jr++) {
-    G.vs[jr] = load_half8(blk + 2 * CB + 512 + 16 * (kb * 4 + jbase + jr));
-    G.vz[jr] = load_half8(blk + 2 * CB + 768 + 16 * (kb * 4 + jbase + jr));
+  G.kc0 = __builtin_bit_cast(uint4, kc0);
+  G.vc0 = __builtin_bit_cast(uint4, vc0);
+  if constexpr (BITS == 4) {
+    G.kc1 = __builtin_bit_cast(uint4, kc1);
+    G.vc1 = __builtin_bit_cast(uint4, vc1);
+  }
+  G.ks = __builtin_bit_cast(half8, ks);
+  G.kz = __builtin_bit_cast(half8, kz);
+  G.vs[0] = __builtin_bit_cast(half8, vs0);
+  G.vz[0] = __builtin_bit_cast(half8, vz0);
+  if constexpr (NJ == 2) {
+    G.vs[1] = __builtin_bit_cast(half8, vs1);
+    G.vz[1] = __builtin_bit_cast(half8, vz1);
   }
 }
 
@@ -404,17 +451,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     struct {
       half8 b[4][U][4];  // key-side B operands per wave: [kc][column kind][k-block]
     } bk[kWaves];
-    float ts[HG][kG];  // FP16-window scores / weights of one chunk
   } sh;
   static_assert(NBUF * GB >= HG * kPartialStride * 4, "wave partial must fit in the wave's ring");
   const WaveParts wp{reinterpret_cast<float*>(&ring[0][0]), NBUF * GB / 4};
 
-  // 1-D grid: one FP16-window workgroup per (sequence, kv-head) first, then nsplit
-  // workgroups per (sequence, kv-head) over its quantized groups.
-  const int nwin = a.B * a.Hkv;
+  // 1-D grid: wblocks FP16-window workgroups per (sequence, kv-head) first, then
+  // nsplit workgroups per (sequence, kv-head) over its quantized groups.
+  const int nwin = a.B * a.Hkv * a.wblocks;
   const bool tail = int(blockIdx.x) < nwin;
-  const int bh = tail ? int(blockIdx.x) : (int(blockIdx.x) - nwin) / a.nsplit;
-  const int split = tail ? a.nsplit : (int(blockIdx.x) - nwin) % a.nsplit;
+  const int bh = tail ? int(blockIdx.x) / a.wblocks : (int(blockIdx.x) - nwin) / a.nsplit;
+  const int split = tail ? a.nsplit + int(blockIdx.x) % a.wblocks : (int(blockIdx.x) - nwin) % a.nsplit;
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const SeqDesc sd = a.seq[b];
@@ -428,7 +474,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int per = (len + kWaves - 1) / kWaves;
   const int wg0 = g0 + wave * per;
   const int wg1 = min(g1, wg0 + per);
-  const int n = tail ? 0 : max(0, wg1 - wg0);
+  // Wave-uniform (the wave index is), so the loop's waits branch on scalars.
+  const int n = __builtin_amdgcn_readfirstlane(tail ? 0 : max(0, wg1 - wg0));
 
   const uint8_t* base = a.blocks + (size_t(b) * a.Hkv + h) * size_t(a.gcap) * GB;
   uint8_t* myring = &ring[wave][0];
@@ -445,7 +492,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   if (tail || a.rotate) prepare_query<HG>(a, b, h, qf, expo);
 
   if (tail) {
-    tail_window<HG>(a, b, h, Q, T, qf, expo, sh.ts, wp);
+    // Window workgroup wsub takes chunks 4 * wsub + wave of the window [Q, T).
+    const int chunk = (split - a.nsplit) * kWaves + wave;
+    const int t0 = Q + chunk * kG;
+    window_chunk<HG>(a, b, h, t0, min(kG, T - t0), qf, expo, wp, wave, lane);
     merge_and_store<HG>(a, b, h, split, wp);
     return;
   }
@@ -496,6 +546,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const float exp_ = partner<U>(exh);
     ex = ishi ? exh : exp_;
   }
+  half8 qh16[ITEMS];  // fp16 copies of qreg for the high parts of the key-side operand
+  for (int it = 0; it < ITEMS; it++) qh16[it] = to_half8(qreg[it]);
 
   float4v oacc[8];
   for (int t = 0; t < 8; t++) oacc[t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -516,7 +568,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int it = 0; it < ITEMS; it++) {
       const int hh = hh0 + 4 * it;
       half8 hi, lo;
-      split_products(qreg[it], g.ks, hi, lo);
+      split_products(qreg[it], qh16[it], g.ks, hi, lo);
       float z = 0.0f;
       for (int s = 0; s < 8; s++) z = __builtin_fmaf(qreg[it][s], float(g.kz[s]), z);
       qz[it] = wave_sum_rows(row_sum_stride4(z));
@@ -568,9 +620,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       l_run += p[i];
     }
     // Value side: B = p * s_value (fp16 high + low parts), plus sum p * z_value.
+    const half8 ph = to_half8(p);
     half8 bvh[NJ], bvl[NJ];
     for (int jr = 0; jr < NJ; jr++) {
-      split_products(p, g.vs[jr], bvh[jr], bvl[jr]);
+      split_products(p, ph, g.vs[jr], bvh[jr], bvl[jr]);
       float z = zacc[jr];
       for (int s = 0; s < 8; s++) z = __builtin_fmaf(p[s], float(g.vz[jr][s]), z);
       zacc[jr] = z;
@@ -625,7 +678,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // slices of 16 threads sum strided subsets of the partials.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineChannels = 16;
-constexpr int kCombineMaxParts = kMaxSplits + 1;
+constexpr int kCombineMaxParts = kMaxSplits + kMaxWindowBlocks;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part,
                                                                   float* __restrict__ out, int Hq, int nparts) {
@@ -688,7 +741,7 @@ int resident_blocks_of() {
 
 template <int BITS, int HG>
 hipError_t launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<BITS, HG>), dim3((a.nsplit + 1) * a.Hkv * B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<BITS, HG>), dim3((a.nsplit + a.wblocks) * a.Hkv * B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -717,6 +770,7 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   a.W = L.W;
   a.gps = groups_per_split;
   a.nsplit = nsplit;
+  a.wblocks = L.win_blocks;
   a.B = L.B;
   a.rotate = rotate;
   a.scale_log2 = scale_log2;
@@ -736,7 +790,7 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   }
   if (e != hipSuccess) return e;
   if (prof_stop && hipEventRecord(prof_stop, stream) != hipSuccess) return hipGetLastError();
-  hipLaunchKernelGGL(combine_kernel, dim3(L.Hq, L.B, kD / kCombineChannels), dim3(kCombineThreads), 0, stream, a.part, out, L.Hq, a.nsplit + 1);
+  hipLaunchKernelGGL(combine_kernel, dim3(L.Hq, L.B, kD / kCombineChannels), dim3(kCombineThreads), 0, stream, a.part, out, L.Hq, a.nsplit + a.wblocks);
   return hipGetLastError();
 }
 

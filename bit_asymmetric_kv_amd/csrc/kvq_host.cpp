@@ -83,6 +83,8 @@ Layout make_layout(const kvq_config* cfg) {
   L.group_bytes = kvq_group_bytes(cfg->bits);
   int64_t ms = (L.gcap + kvq::kMinGroupsPerSplit - 1) / kvq::kMinGroupsPerSplit;
   L.max_splits = int32_t(std::max<int64_t>(1, std::min<int64_t>(ms, kvq::kMaxSplits)));
+  const int32_t win_chunks = L.R / kvq::kGroup + 1;  // the window holds < R + G tokens
+  L.win_blocks = (win_chunks + kvq::kWindowChunksPerBlock - 1) / kvq::kWindowChunksPerBlock;
   size_t off = 0;
   L.seq_off = off;
   off = align256(off + sizeof(SeqDesc) * size_t(L.B));
@@ -94,7 +96,7 @@ Layout make_layout(const kvq_config* cfg) {
   L.ringv_off = off;
   off = align256(off + ring);
   L.part_off = off;
-  off = align256(off + size_t(L.B) * L.Hq * size_t(L.max_splits + 1) * kvq::kPartialStride * 4);
+  off = align256(off + size_t(L.B) * L.Hq * size_t(L.max_splits + L.win_blocks) * kvq::kPartialStride * 4);
   L.total = off;
   return L;
 }
@@ -312,7 +314,8 @@ kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, hipStre
       c->resident_blocks = std::max(1, kvq::decode_resident_blocks(c->cfg.bits,
                                                                    c->cfg.num_q_heads / c->cfg.num_kv_heads));
     const int64_t bh = int64_t(c->cfg.batch) * c->cfg.num_kv_heads;
-    const int64_t slots = std::max<int64_t>(bh, c->resident_blocks - std::min<int64_t>(bh, c->resident_blocks / 4));
+    const int64_t win = bh * c->L.win_blocks;
+    const int64_t slots = std::max<int64_t>(bh, c->resident_blocks - std::min<int64_t>(win, c->resident_blocks / 4));
     const int64_t splits = std::max<int64_t>(1, slots / bh);
     gps = std::max<int64_t>(kvq::kMinGroupsPerSplit, (max_groups + splits - 1) / splits);
   }

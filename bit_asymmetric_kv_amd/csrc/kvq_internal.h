@@ -11,7 +11,11 @@ constexpr int kGroup = 32;
 constexpr int kPartialStride = kHeadDim + 2;  // m (log2 domain), l, o[128] per partial
 constexpr int kMinGroupsPerSplit = 4;
 constexpr int kMaxSplits = 2048;
-constexpr int kMaxResidual = 4096;  // FP16 window chunks: residual / 32 + 1 per (b, h)
+constexpr int kMaxResidual = 4096;
+// The FP16 window [Q, T) holds at most residual + group - 1 tokens: residual / 32 + 1
+// chunks of 32 tokens, four per decode workgroup.
+constexpr int kWindowChunksPerBlock = 4;
+constexpr int kMaxWindowBlocks = (kMaxResidual / kGroup + 1 + kWindowChunksPerBlock - 1) / kWindowChunksPerBlock;
 
 // Per-sequence record kept on the device and rewritten by every append:
 // tokens before the append, tokens appended, quantized tokens before and after.
@@ -39,6 +43,7 @@ struct Layout {
   int64_t gcap;                     // group blocks per (b, h)
   size_t group_bytes;
   int32_t max_splits;
+  int32_t win_blocks;  // FP16-window decode workgroups per (b, h)
   size_t seq_off, blocks_off, ringk_off, ringv_off, part_off, total;
 };
 
