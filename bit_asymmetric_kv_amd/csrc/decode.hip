@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int NJ = NCOPY >= 4 ? 1 : 4 / NCOPY;  // value channel groups handled per lane
   constexpr int GB = 2 * (kG * kD * BITS / 8) + 1024;
   constexpr int LPG = GB / 1024;              // 16-byte-per-lane loads per group block
-  constexpr int NBUF = 3;                     // group blocks per wave in shared memory
+  constexpr int NBUF = 2;                     // group blocks per wave in shared memory
   constexpr int ITEMS = (HG + 3) / 4;         // key-side operand items per lane
 
   // Each wave streams its group blocks HBM -> shared memory with direct loads into a
@@ -561,9 +561,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   GroupRegs<BITS, NJ> G;   // group whose scores are in s0 / s1
   float4v s0, s1;
 
-  auto key_side = [&](const GroupRegs<BITS, NJ>& g, float4v& r0, float4v& r1) {
-    // q' = q * s_key per channel as fp16 high + low parts, through shared memory into
-    // the MFMA B layout; q . z_key per head.
+  // Key side, first half: q' = q * s_key per channel as fp16 high + low parts, to
+  // shared memory in the MFMA B layout, and q . z_key per head (returned for this
+  // lane's column). Issued one group ahead so that its shared-memory round trips
+  // overlap the previous group's value side.
+  auto key_prep = [&](const GroupRegs<BITS, NJ>& g) -> float {
     float qz[ITEMS];
     for (int it = 0; it < ITEMS; it++) {
       const int hh = hh0 + 4 * it;
@@ -577,14 +579,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         sh.bk[wave].b[cb / 4][U - 1 - hh][cb % 4] = lo;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float qzc;
     if constexpr (ITEMS == 1) qzc = qz[0];
     else qzc = hd >= 4 ? qz[1] : qz[0];
-    if (!ishi) qzc = 0.0f;  // q . z_key enters once, through the high-part column
-    // Scores of the group's 32 tokens: rows 4*kb + i of token tiles 0 and 1.
+    return ishi ? qzc : 0.0f;  // q . z_key enters once, through the high-part column
+  };
+  // Key side, second half: scores of the group's 32 tokens (rows 4*kb + i of token
+  // tiles 0 and 1); the high and low parts are added across the paired columns.
+  auto key_mfma = [&](const GroupRegs<BITS, NJ>& g, float qzc, float4v& r0, float4v& r1) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     r0 = float4v{qzc, qzc, qzc, qzc};
     r1 = r0;
     for (int kc = 0; kc < 4; kc++) {
@@ -641,15 +646,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     wait_group_loads<LPG, NBUF>(min(NBUF - 2, n - 1));
     read_group<BITS, NJ>(G, myring, lane, cb, kb, jbase);
     if (NBUF - 1 < n) issue(NBUF - 1);
-    key_side(G, s0, s1);
+    key_mfma(G, key_prep(G), s0, s1);
   }
   for (int r = 0; r + 1 < n; r++) {
     GroupRegs<BITS, NJ> Gn;
     wait_group_loads<LPG, NBUF>(min(NBUF - 2, n - 2 - r));
     read_group<BITS, NJ>(Gn, myring + ((r + 1) % NBUF) * GB, lane, cb, kb, jbase);
     if (r + NBUF < n) issue(r + NBUF);
+    const float qzn = key_prep(Gn);
     value_side(G, s0, s1);
-    key_side(Gn, s0, s1);
+    key_mfma(Gn, qzn, s0, s1);
     G = Gn;
   }
   if (n > 0) value_side(G, s0, s1);
