@@ -449,7 +449,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ float expo[HG];
   __shared__ union {
     struct {
-      half8 b[4][U][4];  // key-side B operands per wave: [kc][column kind][k-block]
+      // key-side B operands per wave: [kc][k-block][column kind, rotated by
+      // (U / 2) * k-block so that neither the writes nor the reads collide in banks]
+      half8 b[4][4][U];
     } bk[kWaves];
   } sh;
   static_assert(NBUF * GB >= HG * kPartialStride * 4, "wave partial must fit in the wave's ring");
@@ -575,8 +577,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       for (int s = 0; s < 8; s++) z = __builtin_fmaf(qreg[it][s], float(g.kz[s]), z);
       qz[it] = wave_sum_rows(row_sum_stride4(z));
       if (bwriter) {
-        sh.bk[wave].b[cb / 4][hh][cb % 4] = hi;
-        sh.bk[wave].b[cb / 4][U - 1 - hh][cb % 4] = lo;
+        const int rot = (U / 2) * (cb % 4);
+        sh.bk[wave].b[cb / 4][cb % 4][(hh + rot) % U] = hi;
+        sh.bk[wave].b[cb / 4][cb % 4][(U - 1 - hh + rot) % U] = lo;
       }
     }
     float qzc;
@@ -593,7 +596,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     r0 = float4v{qzc, qzc, qzc, qzc};
     r1 = r0;
     for (int kc = 0; kc < 4; kc++) {
-      const half8 bk = sh.bk[wave].b[kc][u][kb];
+      const half8 bk = sh.bk[wave].b[kc][kb][(u + (U / 2) * kb) % U];
       r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(g.kc0, g.kc1, 2 * kc), bk, r0, 0, 0, 0);
       r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(g.kc0, g.kc1, 2 * kc + 1), bk, r1, 0, 0, 0);
     }
@@ -679,56 +682,50 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 }
 
 // out[b][hq][d] = sum_i o_i[d] 2^(m_i - M) / sum_i l_i 2^(m_i - M) over the
-// partials of one (sequence, query head). One workgroup per (query head, sequence,
-// 16-channel slice): the weights 2^(m_i - M) go to shared memory once, then 16
-// slices of 16 threads sum strided subsets of the partials.
+// partials of one (sequence, query head), M = max_i m_i. One workgroup per (query
+// head, sequence, 16-channel slice): 16 slices of 16 threads each merge a strided
+// subset of the partials with a running maximum (all of a thread's loads are
+// independent, so the partials are read in one memory round trip), then the slices
+// are merged in shared memory.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineChannels = 16;
-constexpr int kCombineMaxParts = kMaxSplits + kMaxWindowBlocks;
+constexpr int kCombineSlices = kCombineThreads / kCombineChannels;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part,
                                                                   float* __restrict__ out, int Hq, int nparts) {
-  __shared__ float wgt[kCombineMaxParts];
-  __shared__ float red[kCombineThreads / 64];
-  __shared__ float osum[kCombineThreads / kCombineChannels][kCombineChannels];
+  __shared__ float sm[kCombineSlices], sl[kCombineSlices];
+  __shared__ float so[kCombineSlices][kCombineChannels];
   const int hq = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z * kCombineChannels, tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int dl = tid % kCombineChannels, slice = tid / kCombineChannels;
   const float* p = part + (size_t(b) * Hq + hq) * size_t(nparts) * kPartialStride;
 
-  float m = -INFINITY;
-  for (int i = tid; i < nparts; i += kCombineThreads) m = fmaxf(m, p[size_t(i) * kPartialStride]);
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  float M = red[0];
-  for (int w = 1; w < kCombineThreads / 64; w++) M = fmaxf(M, red[w]);
-  __syncthreads();
-
-  float l = 0.0f;
-  for (int i = tid; i < nparts; i += kCombineThreads) {
-    const float mi = p[size_t(i) * kPartialStride];
-    const float wi = mi == -INFINITY ? 0.0f : exp2f(mi - M);
-    wgt[i] = wi;
-    l += wi * p[size_t(i) * kPartialStride + 1];
+  float m = -INFINITY, l = 0.0f, o = 0.0f;
+  for (int i = slice; i < nparts; i += kCombineSlices) {
+    const float* pi = p + size_t(i) * kPartialStride;
+    const float mi = pi[0], li = pi[1], oi = pi[2 + d0 + dl];
+    if (mi == -INFINITY) continue;
+    const float mn = fmaxf(m, mi);
+    const float a = m == -INFINITY ? 0.0f : exp2f(m - mn), c = exp2f(mi - mn);
+    l = l * a + li * c;
+    o = o * a + oi * c;
+    m = mn;
   }
-  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-  if (lane == 0) red[wave] = l;
-  __syncthreads();
-  float L = 0.0f;
-  for (int w = 0; w < kCombineThreads / 64; w++) L += red[w];
-
-  constexpr int kSlices = kCombineThreads / kCombineChannels;
-  const int dl = tid % kCombineChannels, slice = tid / kCombineChannels;
-  float o = 0.0f;
-  for (int i = slice; i < nparts; i += kSlices) {
-    const float wi = wgt[i];
-    if (wi != 0.0f) o += wi * p[size_t(i) * kPartialStride + 2 + d0 + dl];
+  if (dl == 0) {
+    sm[slice] = m;
+    sl[slice] = l;
   }
-  osum[slice][dl] = o;
+  so[slice][dl] = o;
   __syncthreads();
   if (slice == 0) {
-    float acc = 0.0f;
-    for (int s2 = 0; s2 < kSlices; s2++) acc += osum[s2][dl];
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < kCombineSlices; s2++) M = fmaxf(M, sm[s2]);
+    float L = 0.0f, acc = 0.0f;
+    for (int s2 = 0; s2 < kCombineSlices; s2++) {
+      if (sm[s2] == -INFINITY) continue;
+      const float w = exp2f(sm[s2] - M);
+      L += sl[s2] * w;
+      acc += so[s2][dl] * w;
+    }
     out[(size_t(b) * Hq + hq) * kD + d0 + dl] = acc / L;
   }
 }
