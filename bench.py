@@ -140,6 +140,59 @@ def cpu_baseline(w, heads=4, steps=3):
                       f"{dt:.1f} s timed, numpy with one BLAS thread"}
 
 
+def measure_comparisons(torch, kvq, w, ev, stream, dev, iters=20):
+    """Achievable HBM read bandwidth (streaming-read probe over 2 GiB) and the FP16-
+    cache decode on the workload's shapes (same tokens per sequence, two caches
+    round-robin), each timed with one pair of HIP events around `iters` calls."""
+    res = {}
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        kvq.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    a, b = ev.create(1)[0], ev.create(1)[0]
+    ev.record(a, stream)
+    for _ in range(iters):
+        kvq.stream_read(buf, sink)
+    ev.record(b, stream)
+    torch.cuda.synchronize()
+    res["hbm_stream_read_gbps"] = round(buf.numel() * iters / (ev.elapsed_ms(a, b) * 1e-3) / 1e9, 1)
+    del buf
+
+    lens = w.context_lengths() + 1
+    t_cap = int(lens.max())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed * 31)
+    shape = (w.batch, w.num_kv_heads, t_cap, w.head_dim)
+    caches = []
+    for _ in range(2):
+        k = torch.randn(shape, generator=gen, device=dev).to(torch.float16)
+        v = torch.randn(shape, generator=gen, device=dev).to(torch.float16)
+        caches.append((k, v))
+    lens_dev = torch.tensor(lens.astype(np.int32), device=dev)
+    q = torch.randn((w.batch, w.num_q_heads, w.head_dim), generator=gen, device=dev).to(torch.float16)
+    op = kvq.Fp16Decode(w.batch, w.num_q_heads, w.num_kv_heads, t_cap, device=dev)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    for i in range(4):
+        op(*caches[i % 2], lens_dev, t_cap, q, out)
+    torch.cuda.synchronize()
+    ev.record(a, stream)
+    for i in range(iters):
+        op(*caches[i % 2], lens_dev, t_cap, q, out)
+    ev.record(b, stream)
+    torch.cuda.synchronize()
+    us = ev.elapsed_ms(a, b) / iters * 1e3
+    fp16_bytes = int(lens.sum()) * w.num_kv_heads * 2 * 2 * w.head_dim
+    res.update({"fp16_decode_us": round(us, 2), "fp16_cache_bytes": fp16_bytes,
+                "fp16_decode_gbps": round(fp16_bytes / (us * 1e-6) / 1e9, 1),
+                "fp16_outputs_finite": bool(torch.isfinite(out).all())})
+    ev.destroy([a, b])
+    del caches
+    torch.cuda.synchronize()
+    return res
+
+
 COPY_BYTES = 1 << 30
 KERNEL_SOURCE = os.path.join(ROOT, "bit_asymmetric_kv_amd", "csrc", "decode.hip")
 
@@ -215,6 +268,8 @@ def main():
     ap.add_argument("--copies", type=int, default=8, help="independent caches stepped round-robin")
     ap.add_argument("--groups-per-split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-comparisons", action="store_true",
+                    help="skip the streaming-read probe and the FP16-cache decode")
     ap.add_argument("--warm-iters", type=int, default=30,
                     help="extra decode calls on one cache to report a last-level-cache-resident time (0: skip)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -316,6 +371,16 @@ def main():
         except (OSError, ValueError):
             traffic = None
 
+    comp = None
+    if not args.no_comparisons:
+        print("[bench] streaming-read probe and FP16-cache decode", file=sys.stderr, flush=True)
+        for c in caches:
+            c.close()
+        del caches
+        torch.cuda.empty_cache()
+        comp = measure_comparisons(torch, kvq, w, ev, stream, dev)
+        comp["quantized_decode_speedup_vs_fp16"] = round(comp["fp16_decode_us"] / (kern_avg_ms * 1e3), 2)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -338,7 +403,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "context": int(w.context_lengths().max()), "bits": w.bits,
                    "group": w.group, "residual": w.residual, "rotate": w.rotate,
-                   "caches_round_robin": len(caches), "parallelism": "single GPU"},
+                   "caches_round_robin": args.copies, "parallelism": "single GPU"},
         "step": {"algorithmic_bytes": int(bytes_avg), "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
                  "decode_split_kernel_us": round(kern_avg_ms * 1e3, 2),
                  "decode_split_kernel_p10_p50_p90_us": [round(float(np.percentile(kern_ms, p)) * 1e3, 2)
@@ -349,7 +414,10 @@ def main():
                  "outputs_finite": out_ok},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": f"decode_split_kernel<{w.bits},{w.num_q_heads // w.num_kv_heads}>"},
+                     "kernel": f"decode_split_kernel<{w.bits},{w.num_q_heads // w.num_kv_heads}>",
+                     "frac_of_measured_stream_read": (round(achieved / comp["hbm_stream_read_gbps"], 4)
+                                                      if comp else None)},
+        "comparison": comp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -3,5 +3,5 @@
 The compute path is the HIP library libkvq.so (C ABI in include/kvq.h); this
 package only binds it.
 """
-from ._lib import (KVCache, KVQConfig, KVQError, cache_bytes, group_bytes, load,  # noqa: F401
-                   make_config)
+from ._lib import (Fp16Decode, KVCache, KVQConfig, KVQError, cache_bytes, group_bytes, load,  # noqa: F401
+                   make_config, stream_read)

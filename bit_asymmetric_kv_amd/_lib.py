@@ -30,7 +30,7 @@ KVQ_PART_RING_V = 2
 EXPORTED = (
     "kvq_cache_bytes", "kvq_create", "kvq_append", "kvq_decode_attention", "kvq_set_decode_split",
     "kvq_destroy", "kvq_seq_len", "kvq_group_bytes", "kvq_read_state", "kvq_last_error",
-    "kvq_set_profile_events",
+    "kvq_set_profile_events", "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention",
 )
 
 
@@ -45,6 +45,17 @@ class KVQConfig(ctypes.Structure):
         ("residual", ctypes.c_int32),
         ("rotate", ctypes.c_int32),
         ("max_tokens", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class KVQFp16Config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("t_cap", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float),
     ]
 
@@ -82,8 +93,13 @@ def load() -> ctypes.CDLL:
     lib.kvq_read_state.argtypes = [vp, i32, i32, i32, sz, vp, sz, vp]
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
+    f16p = ctypes.POINTER(KVQFp16Config)
+    lib.kvq_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.kvq_fp16_workspace_bytes.argtypes = [f16p, ctypes.POINTER(sz)]
+    lib.kvq_fp16_decode_attention.argtypes = [f16p, vp, vp, vp, i64, vp, vp, vp, sz, vp]
     for name in ("kvq_cache_bytes", "kvq_create", "kvq_append", "kvq_decode_attention",
-                 "kvq_set_decode_split", "kvq_seq_len", "kvq_read_state", "kvq_set_profile_events"):
+                 "kvq_set_decode_split", "kvq_seq_len", "kvq_read_state", "kvq_set_profile_events",
+                 "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -225,3 +241,46 @@ class KVCache:
             self.close()
         except Exception:
             pass
+
+
+# -- comparison kernels -------------------------------------------------------
+
+def stream_read(buf, sink):
+    """Stream-read every byte of the device tensor `buf` once; xor a fold into the
+    int32 device tensor `sink` (one element). Asynchronous on the current stream."""
+    import torch
+    check(load().kvq_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                 ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(torch, buf.device))))
+
+
+class Fp16Decode:
+    """Decode attention over a plain FP16 cache k, v [B, Hkv, t_cap, D] (comparison
+    baseline of the quantized path). Owns its workspace as a torch tensor."""
+
+    def __init__(self, batch, num_q_heads, num_kv_heads, t_cap, head_dim=128, softmax_scale=0.0, device="cuda"):
+        import torch
+        self._torch = torch
+        self.device = torch.device(device)
+        self.cfg = KVQFp16Config(batch, num_q_heads, num_kv_heads, head_dim, t_cap, softmax_scale)
+        nbytes = ctypes.c_size_t(0)
+        check(load().kvq_fp16_workspace_bytes(ctypes.byref(self.cfg), ctypes.byref(nbytes)))
+        self.workspace = torch.empty(nbytes.value, dtype=torch.uint8, device=self.device)
+
+    def __call__(self, k, v, seq_lens, max_len, q, out=None):
+        """k, v: fp16 [B, Hkv, t_cap, D]; seq_lens: int32 [B] on the device; q: fp16 [B, Hq, D]."""
+        torch = self._torch
+        c = self.cfg
+        for t, shape, dt, name in ((k, (c.batch, c.num_kv_heads, c.t_cap, c.head_dim), torch.float16, "k"),
+                                   (v, (c.batch, c.num_kv_heads, c.t_cap, c.head_dim), torch.float16, "v"),
+                                   (seq_lens, (c.batch,), torch.int32, "seq_lens"),
+                                   (q, (c.batch, c.num_q_heads, c.head_dim), torch.float16, "q")):
+            if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name} must be a contiguous {dt} device tensor of shape {shape}")
+        if out is None:
+            out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=torch.float32, device=self.device)
+        check(load().kvq_fp16_decode_attention(
+            ctypes.byref(c), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+            ctypes.c_void_p(seq_lens.data_ptr()), int(max_len), ctypes.c_void_p(q.data_ptr()),
+            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(self.workspace.data_ptr()),
+            self.workspace.numel(), ctypes.c_void_p(_stream_ptr(torch, self.device))))
+        return out

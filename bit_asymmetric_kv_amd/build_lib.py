@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["kvq_host.cpp", "append.hip", "decode.hip"]
+SOURCES = ["kvq_host.cpp", "append.hip", "decode.hip", "baseline.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

@@ -793,7 +793,12 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   }
   if (e != hipSuccess) return e;
   if (prof_stop && hipEventRecord(prof_stop, stream) != hipSuccess) return hipGetLastError();
-  hipLaunchKernelGGL(combine_kernel, dim3(L.Hq, L.B, kD / kCombineChannels), dim3(kCombineThreads), 0, stream, a.part, out, L.Hq, a.nsplit + a.wblocks);
+  return launch_combine(a.part, out, L.Hq, L.B, a.nsplit + a.wblocks, stream);
+}
+
+hipError_t launch_combine(const float* part, float* out, int Hq, int B, int nparts, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_kernel, dim3(Hq, B, kD / kCombineChannels), dim3(kCombineThreads), 0, stream, part, out,
+                     Hq, nparts);
   return hipGetLastError();
 }
 

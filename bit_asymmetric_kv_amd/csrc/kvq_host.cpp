@@ -365,4 +365,77 @@ kvq_status kvq_read_state(kvq_cache* c, int32_t part, int32_t b, int32_t h, size
   return ok();
 }
 
+kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink) return fail(KVQ_ERR_INVALID_ARG, "buf and sink must be device pointers");
+  if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(KVQ_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and buf 16-byte aligned");
+  int ndev = 0, dev = 0, cus = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return fail(KVQ_ERR_NO_DEVICE, "no HIP device available");
+  }
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(KVQ_ERR_HIP, "device query failed: %s", hipGetErrorString(hipGetLastError()));
+  const size_t n16 = bytes / 16;
+  const size_t want = (n16 + 4 * 256 - 1) / (4 * 256);  // about 4 words per thread per pass
+  const int blocks = int(std::max<size_t>(1, std::min<size_t>(want, size_t(cus) * 8)));
+  const hipError_t e = kvq::launch_stream_read(buf, bytes, sink, blocks, stream);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "stream read launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kvq_status kvq_fp16_workspace_bytes(const kvq_fp16_config* cfg, size_t* bytes) {
+  if (!cfg || !bytes) return fail(KVQ_ERR_INVALID_ARG, "cfg and bytes must not be NULL");
+  if (cfg->batch < 1 || cfg->num_kv_heads < 1 || cfg->num_q_heads < 1 || cfg->num_q_heads % cfg->num_kv_heads)
+    return fail(KVQ_ERR_INVALID_ARG, "need batch >= 1 and num_q_heads a positive multiple of num_kv_heads");
+  *bytes = size_t(cfg->batch) * cfg->num_q_heads * kvq::kFp16MaxSplits * kvq::kPartialStride * 4;
+  return ok();
+}
+
+kvq_status kvq_fp16_decode_attention(const kvq_fp16_config* cfg, const void* k, const void* v,
+                                     const int32_t* seq_lens, int64_t max_len, const void* q, float* out,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!cfg) return fail(KVQ_ERR_INVALID_ARG, "cfg is NULL");
+  const int ratio = cfg->num_kv_heads > 0 ? cfg->num_q_heads / cfg->num_kv_heads : 0;
+  if (cfg->batch < 1 || cfg->num_kv_heads < 1 || cfg->num_q_heads % cfg->num_kv_heads != 0 ||
+      !(ratio == 1 || ratio == 2 || ratio == 4 || ratio == 8))
+    return fail(KVQ_ERR_INVALID_ARG, "batch >= 1 and num_q_heads / num_kv_heads in {1, 2, 4, 8} required");
+  if (cfg->head_dim != kvq::kHeadDim) return fail(KVQ_ERR_INVALID_ARG, "head_dim must be 128");
+  if (cfg->t_cap < 1 || cfg->t_cap > (int64_t(1) << 30))
+    return fail(KVQ_ERR_INVALID_ARG, "t_cap must be in [1, 2^30]");
+  if (max_len < 1 || max_len > cfg->t_cap)
+    return fail(KVQ_ERR_INVALID_ARG, "max_len must be in [1, t_cap]");
+  if (!k || !v || !seq_lens || !q || !out || !workspace)
+    return fail(KVQ_ERR_INVALID_ARG, "k, v, seq_lens, q, out and workspace must be device pointers");
+  size_t need = 0;
+  kvq_status st = kvq_fp16_workspace_bytes(cfg, &need);
+  if (st != KVQ_OK) return st;
+  if (workspace_bytes < need) return fail(KVQ_ERR_OOM, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  int ndev = 0, dev = 0, cus = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return fail(KVQ_ERR_NO_DEVICE, "no HIP device available");
+  }
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(KVQ_ERR_HIP, "device query failed: %s", hipGetErrorString(hipGetLastError()));
+  // About four workgroups per compute unit in one round, at least one chunk per wave.
+  const int64_t bh = int64_t(cfg->batch) * cfg->num_kv_heads;
+  const int64_t nch = (max_len + 31) / 32;
+  int64_t splits = std::max<int64_t>(1, (int64_t(cus) * 4) / bh);
+  int64_t cps = std::max<int64_t>(4, (nch + splits - 1) / splits);
+  int64_t nsplit = (nch + cps - 1) / cps;
+  if (nsplit > kvq::kFp16MaxSplits) {
+    cps = (nch + kvq::kFp16MaxSplits - 1) / kvq::kFp16MaxSplits;
+    nsplit = (nch + cps - 1) / cps;
+  }
+  const float scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / std::sqrt(float(cfg->head_dim));
+  const hipError_t e = kvq::launch_fp16_decode(k, v, seq_lens, cfg->t_cap, cfg->batch, cfg->num_q_heads,
+                                               cfg->num_kv_heads, scale * 1.4426950408889634f, q, out,
+                                               static_cast<float*>(workspace), int(nsplit), int(cps), stream);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "fp16 decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -60,4 +60,15 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
                          float* out, int32_t groups_per_split, int32_t nsplit, float scale_log2,
                          int rotate, hipStream_t stream, hipEvent_t prof_start, hipEvent_t prof_stop);
 
+// Merge nparts partials per (sequence, query head) laid out [B][Hq][nparts][130].
+hipError_t launch_combine(const float* part, float* out, int Hq, int B, int nparts, hipStream_t stream);
+
+// Comparison kernels: streaming read of a buffer; decode over a plain FP16 cache
+// [B][Hkv][t_cap][128] (partials [B][Hq][nsplit][130] in `part`).
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
+hipError_t launch_fp16_decode(const void* k, const void* v, const int32_t* lens, long long t_cap, int B, int Hq,
+                              int Hkv, float scale_log2, const void* q, float* out, float* part, int nsplit,
+                              int cps, hipStream_t stream);
+constexpr int kFp16MaxSplits = 1024;
+
 }  // namespace kvq

@@ -155,6 +155,46 @@ kvq_status kvq_read_state(kvq_cache* c, int32_t part, int32_t b, int32_t h, size
 /* Message of the last error on this thread ("" if none). */
 const char* kvq_last_error(void);
 
+/* ---- Comparison kernels (measured beside the quantized path, not part of it) ---- */
+
+/* Streaming-read probe: reads each 16-byte word of the device buffer buf[0, bytes)
+ * once with vector loads spread over the whole GPU and xors a fold of the words
+ * into the device word *sink (the caller clears it first if it wants the fold), so
+ * the loads cannot be elided. Timing it gives the achievable HBM read bandwidth to
+ * set the decode kernel's effective bandwidth against (the nominal peak is a
+ * datasheet figure). bytes: positive multiple of 16; buf 16-byte aligned.
+ * Asynchronous on `stream`. */
+kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+/* Decode attention over a plain FP16 KV cache, the full-precision decode that the
+ * pages set low-bit caches against (flash-decoding over the whole cache: "Read
+ * What Matters", the RDKV abstract). Same attention as kvq_decode_attention:
+ * softmax(q.k * softmax_scale) over tokens [0, seq_lens[b]) of sequence b, query
+ * head hq reading KV head hq / (num_q_heads / num_kv_heads); no rotation. */
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t num_q_heads;  /* Hq; Hq / Hkv in {1, 2, 4, 8} */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* must be 128 */
+  int64_t t_cap;        /* token capacity per (b, h) of k and v, 1 .. 2^30 */
+  float softmax_scale;  /* 0 => 1/sqrt(head_dim) */
+} kvq_fp16_config;
+
+/* Bytes of device workspace kvq_fp16_decode_attention needs (host only). */
+kvq_status kvq_fp16_workspace_bytes(const kvq_fp16_config* cfg, size_t* bytes);
+
+/*  k, v:     device fp16 [B][Hkv][t_cap][D], token t of (b, h) at row t
+ *  seq_lens: device int32 [B], 1 <= seq_lens[b] <= max_len (read by the kernels;
+ *            values above t_cap are clamped to t_cap)
+ *  max_len:  host upper bound of seq_lens, 1 <= max_len <= t_cap (sizes the grid)
+ *  q:        device fp16 [B][Hq][D];  out: device fp32 [B][Hq][D]
+ *  workspace: device buffer of at least kvq_fp16_workspace_bytes() bytes, owned by
+ *            the caller; calls sharing a workspace must not overlap.
+ * Asynchronous on `stream`. */
+kvq_status kvq_fp16_decode_attention(const kvq_fp16_config* cfg, const void* k, const void* v,
+                                     const int32_t* seq_lens, int64_t max_len, const void* q, float* out,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

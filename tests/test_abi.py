@@ -13,7 +13,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -86,3 +86,31 @@ def test_cache_bytes_grows_with_capacity_and_holds_the_blocks():
     assert big >= 8 * 32768 * 3072
     four = kvq.cache_bytes(kvq.make_config(1, 32, 8, bits=4, residual=128, max_tokens=131072))
     assert four - small >= 8 * 4096 * (5120 - 3072)
+
+
+def test_comparison_entry_points_validate_on_the_host():
+    lib = kvq.load()
+    cfg = _lib.KVQFp16Config(1, 32, 8, 128, 4096, 0.0)
+    n = ctypes.c_size_t(0)
+    assert lib.kvq_fp16_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == _lib.KVQ_OK
+    assert n.value == 1 * 32 * 1024 * 130 * 4
+    bad = _lib.KVQFp16Config(1, 12, 8, 128, 4096, 0.0)   # Hq not a multiple of Hkv
+    assert lib.kvq_fp16_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == _lib.KVQ_ERR_INVALID_ARG
+    fake = ctypes.c_void_p(256)   # never dereferenced: every check below fails first
+    # head_dim other than 128
+    c2 = _lib.KVQFp16Config(1, 32, 8, 64, 4096, 0.0)
+    assert lib.kvq_fp16_decode_attention(ctypes.byref(c2), fake, fake, fake, 10, fake, fake, fake, 1 << 30,
+                                         None) == _lib.KVQ_ERR_INVALID_ARG
+    # max_len above t_cap
+    assert lib.kvq_fp16_decode_attention(ctypes.byref(cfg), fake, fake, fake, 4097, fake, fake, fake, 1 << 30,
+                                         None) == _lib.KVQ_ERR_INVALID_ARG
+    # workspace too small
+    assert lib.kvq_fp16_decode_attention(ctypes.byref(cfg), fake, fake, fake, 100, fake, fake, fake, 16,
+                                         None) == _lib.KVQ_ERR_OOM
+    # null pointers
+    assert lib.kvq_fp16_decode_attention(ctypes.byref(cfg), None, fake, fake, 100, fake, fake, fake, 1 << 30,
+                                         None) == _lib.KVQ_ERR_INVALID_ARG
+    # stream read: size not a multiple of 16, misaligned buffer, null sink
+    assert lib.kvq_stream_read(fake, 100, fake, None) == _lib.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_stream_read(ctypes.c_void_p(264), 1024, fake, None) == _lib.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_stream_read(fake, 1024, None, None) == _lib.KVQ_ERR_INVALID_ARG
