@@ -71,18 +71,8 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def gpu_kv(torch, w, mult, off, B, n, gen, dev):
-    """Seeded fp16 keys/values [B, n, Hkv, D] with the workload's distribution."""
-    shape = (B, n, w.num_kv_heads, w.head_dim)
-    k = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
-    k = (mult * (k + off)).to(torch.float16)
-    v = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.float16)
-    return k.contiguous(), v.contiguous()
-
-
 def build_caches(torch, kvq, w, copies, max_tokens, dev, gps):
-    mult = torch.tensor(np.stack([wl.key_channel_params(w, h)[0] for h in range(w.num_kv_heads)]), device=dev)
-    off = torch.tensor(np.stack([wl.key_channel_params(w, h)[1] for h in range(w.num_kv_heads)]), device=dev)
+    params = wl.torch_key_params(torch, w, dev)
     caches = []
     lens = w.context_lengths()
     chunk = 16384
@@ -96,12 +86,12 @@ def build_caches(torch, kvq, w, copies, max_tokens, dev, gps):
         done = np.zeros(w.batch, dtype=np.int64)
         while np.any(done < lens):
             n = np.minimum(lens - done, chunk)
-            k, v = gpu_kv(torch, w, mult, off, w.batch, int(n.max()), gen, dev)
+            k, v = wl.torch_kv(torch, w, params, int(n.max()), gen, dev)
             cache.append(k, v, n.tolist())
             done += n
         caches.append(cache)
     torch.cuda.synchronize()
-    return caches, mult, off
+    return caches, params
 
 
 def step_bytes(cache, w):
@@ -289,13 +279,13 @@ def main():
     total_steps = args.warmup + args.steps
     max_tokens = int(w.context_lengths().max()) + total_steps + 1
     print(f"[bench] building {args.copies} caches of {w.name}", file=sys.stderr, flush=True)
-    caches, mult, off = build_caches(torch, kvq, w, args.copies, max_tokens, dev, args.groups_per_split)
+    caches, params = build_caches(torch, kvq, w, args.copies, max_tokens, dev, args.groups_per_split)
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 7919)
-    knew, vnew = gpu_kv(torch, w, mult, off, total_steps * w.batch, 1, gen, dev)
-    knew = knew.view(total_steps, w.batch, 1, w.num_kv_heads, w.head_dim)
-    vnew = vnew.view(total_steps, w.batch, 1, w.num_kv_heads, w.head_dim)
+    knew, vnew = wl.torch_kv(torch, w, params, total_steps, gen, dev)   # [B, steps, Hkv, D]
+    knew = knew.transpose(0, 1).contiguous().view(total_steps, w.batch, 1, w.num_kv_heads, w.head_dim)
+    vnew = vnew.transpose(0, 1).contiguous().view(total_steps, w.batch, 1, w.num_kv_heads, w.head_dim)
     q = torch.randn((total_steps, w.batch, w.num_q_heads, w.head_dim), generator=gen, device=dev).to(torch.float16)
     outs = [torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev) for _ in caches]
     torch.cuda.synchronize()

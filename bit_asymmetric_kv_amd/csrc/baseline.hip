@@ -209,7 +209,11 @@ hipError_t launch_fp16_decode(const void* k, const void* v, const int32_t* lens,
                  : hg == 4 ? launch_fp16<4>(a, B, stream)
                            : launch_fp16<8>(a, B, stream);
   if (e != hipSuccess) return e;
-  return launch_combine(part, out, Hq, B, nsplit, stream);
+  SplitPlan plan{};
+  plan.use_prefix = 0;
+  plan.uniform = nsplit;
+  plan.pstride = nsplit;
+  return launch_combine(part, out, Hq, B, plan, 0, stream);
 }
 
 }  // namespace kvq

@@ -46,9 +46,9 @@ struct DecodeArgs {
   const __half* q;
   float* part;
   long long gcap;
-  int B, Hkv, Hq, W, gps, nsplit, rotate;
-  int wblocks;  // FP16-window workgroups per (sequence, kv-head); partials per query
-                // head: nsplit (quantized groups) + wblocks (FP16 window)
+  int B, Hkv, Hq, W, gps, rotate;
+  int wblocks;  // FP16-window workgroups per (sequence, kv-head)
+  SplitPlan plan;  // split workgroups per sequence and the partial slots per query head
   float scale_log2;
 };
 
@@ -197,9 +197,14 @@ __device__ void prepare_query(const DecodeArgs& a, int b, int h, float (*qf)[kD]
   __syncthreads();
 }
 
+// Split workgroups of each kv-head of sequence b.
+__device__ inline int splits_of(const SplitPlan& p, int b) {
+  return p.use_prefix ? p.count[b] : p.uniform;
+}
+
 // Partial of one query head: running max m (log2 domain), sum l, output o[128].
 __device__ inline float* partial_ptr(const DecodeArgs& a, int b, int hq, int split) {
-  return a.part + ((size_t(b) * a.Hq + hq) * size_t(a.nsplit + a.wblocks) + split) * kPartialStride;
+  return a.part + ((size_t(b) * a.Hq + hq) * size_t(a.plan.pstride) + split) * kPartialStride;
 }
 
 // Per-wave partials (m, l, o[128] per head) in shared memory; wave w's block starts
@@ -457,13 +462,41 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   static_assert(NBUF * GB >= HG * kPartialStride * 4, "wave partial must fit in the wave's ring");
   const WaveParts wp{reinterpret_cast<float*>(&ring[0][0]), NBUF * GB / 4};
 
-  // 1-D grid: wblocks FP16-window workgroups per (sequence, kv-head) first, then
-  // nsplit workgroups per (sequence, kv-head) over its quantized groups.
-  const int nwin = a.B * a.Hkv * a.wblocks;
-  const bool tail = int(blockIdx.x) < nwin;
-  const int bh = tail ? int(blockIdx.x) / a.wblocks : (int(blockIdx.x) - nwin) / a.nsplit;
-  const int split = tail ? a.nsplit + int(blockIdx.x) % a.wblocks : (int(blockIdx.x) - nwin) % a.nsplit;
-  const int b = bh / a.Hkv, h = bh % a.Hkv;
+  // 1-D grid: the split workgroups first, sequence by sequence in the plan's order
+  // (each sequence's n_b splits for each kv-head), then wblocks FP16-window
+  // workgroups per (sequence, kv-head), which fill the gaps the splits leave.
+  const int nsplit_total = a.plan.use_prefix ? a.plan.prefix[a.B] : a.B * a.plan.uniform;
+  const int wbase = nsplit_total * a.Hkv;
+  const bool tail = int(blockIdx.x) >= wbase;
+  int b, h, split, nsb;
+  if (tail) {
+    const int bh = (int(blockIdx.x) - wbase) / a.wblocks;
+    b = bh / a.Hkv;
+    h = bh % a.Hkv;
+    nsb = splits_of(a.plan, b);
+    split = nsb + (int(blockIdx.x) - wbase) % a.wblocks;
+  } else {
+    const int idx = int(blockIdx.x);
+    if (!a.plan.use_prefix) {
+      nsb = a.plan.uniform;
+      b = idx / (a.Hkv * nsb);
+      const int rem = idx - b * a.Hkv * nsb;
+      h = rem / nsb;
+      split = rem % nsb;
+    } else {
+      int lo = 0, hi = a.B;  // largest position p with Hkv * prefix[p] <= idx
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (a.Hkv * a.plan.prefix[mid] <= idx) lo = mid;
+        else hi = mid;
+      }
+      b = a.plan.seq[lo];
+      nsb = a.plan.prefix[lo + 1] - a.plan.prefix[lo];
+      const int rem = idx - a.Hkv * a.plan.prefix[lo];
+      h = rem / nsb;
+      split = rem % nsb;
+    }
+  }
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const SeqDesc sd = a.seq[b];
   const int T = sd.t_old + sd.n_new, Q = sd.q_new;
@@ -495,7 +528,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   if (tail) {
     // Window workgroup wsub takes chunks 4 * wsub + wave of the window [Q, T).
-    const int chunk = (split - a.nsplit) * kWaves + wave;
+    const int chunk = (split - nsb) * kWaves + wave;
     const int t0 = Q + chunk * kG;
     window_chunk<HG>(a, b, h, t0, min(kG, T - t0), qf, expo, wp, wave, lane);
     merge_and_store<HG>(a, b, h, split, wp);
@@ -692,12 +725,14 @@ constexpr int kCombineChannels = 16;
 constexpr int kCombineSlices = kCombineThreads / kCombineChannels;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part,
-                                                                  float* __restrict__ out, int Hq, int nparts) {
+                                                                  float* __restrict__ out, int Hq,
+                                                                  const SplitPlan plan, int wblocks) {
   __shared__ float sm[kCombineSlices], sl[kCombineSlices];
   __shared__ float so[kCombineSlices][kCombineChannels];
   const int hq = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z * kCombineChannels, tid = threadIdx.x;
   const int dl = tid % kCombineChannels, slice = tid / kCombineChannels;
-  const float* p = part + (size_t(b) * Hq + hq) * size_t(nparts) * kPartialStride;
+  const int nparts = splits_of(plan, b) + wblocks;
+  const float* p = part + (size_t(b) * Hq + hq) * size_t(plan.pstride) * kPartialStride;
 
   float m = -INFINITY, l = 0.0f, o = 0.0f;
   for (int i = slice; i < nparts; i += kCombineSlices) {
@@ -744,7 +779,9 @@ int resident_blocks_of() {
 
 template <int BITS, int HG>
 hipError_t launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<BITS, HG>), dim3((a.nsplit + a.wblocks) * a.Hkv * B), dim3(256), 0, stream, a);
+  const int nsplit_total = a.plan.use_prefix ? a.plan.prefix[B] : B * a.plan.uniform;
+  hipLaunchKernelGGL((decode_split_kernel<BITS, HG>), dim3((nsplit_total + B * a.wblocks) * a.Hkv), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -758,7 +795,8 @@ int decode_resident_blocks(int bits, int hg) {
 }
 
 hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* q, float* out,
-                         int32_t groups_per_split, int32_t nsplit, float scale_log2, int rotate, hipStream_t stream,
+                         int32_t groups_per_split, const SplitPlan& plan, float scale_log2, int rotate,
+                         hipStream_t stream,
                          hipEvent_t prof_start, hipEvent_t prof_stop) {
   DecodeArgs a;
   a.blocks = base + L.blocks_off;
@@ -772,7 +810,7 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   a.Hq = L.Hq;
   a.W = L.W;
   a.gps = groups_per_split;
-  a.nsplit = nsplit;
+  a.plan = plan;
   a.wblocks = L.win_blocks;
   a.B = L.B;
   a.rotate = rotate;
@@ -793,12 +831,13 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   }
   if (e != hipSuccess) return e;
   if (prof_stop && hipEventRecord(prof_stop, stream) != hipSuccess) return hipGetLastError();
-  return launch_combine(a.part, out, L.Hq, L.B, a.nsplit + a.wblocks, stream);
+  return launch_combine(a.part, out, L.Hq, L.B, plan, L.win_blocks, stream);
 }
 
-hipError_t launch_combine(const float* part, float* out, int Hq, int B, int nparts, hipStream_t stream) {
+hipError_t launch_combine(const float* part, float* out, int Hq, int B, const SplitPlan& plan, int wblocks,
+                          hipStream_t stream) {
   hipLaunchKernelGGL(combine_kernel, dim3(Hq, B, kD / kCombineChannels), dim3(kCombineThreads), 0, stream, part, out,
-                     Hq, nparts);
+                     Hq, plan, wblocks);
   return hipGetLastError();
 }
 

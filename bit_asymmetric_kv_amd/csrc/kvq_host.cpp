@@ -301,33 +301,60 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, const int32_t*
 kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, hipStream_t stream) {
   if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
   if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q and out must be device pointers");
-  int64_t max_groups = 0;
-  for (int b = 0; b < c->cfg.batch; b++) {
+  const int B = c->cfg.batch, Hkv = c->cfg.num_kv_heads;
+  int64_t max_groups = 0, sum_groups = 0;
+  for (int b = 0; b < B; b++) {
     if (c->T[b] == 0) return fail(KVQ_ERR_EMPTY, "sequence %d holds no token", b);
     max_groups = std::max(max_groups, c->Q[b] / kvq::kGroup);
+    sum_groups += c->Q[b] / kvq::kGroup;
   }
+  // Equal lengths: one round of equal workgroups. Unequal lengths: about three
+  // rounds of smaller ones, longest sequences first.
+  const bool uniform_lengths = sum_groups == max_groups * B;
   int64_t gps = c->groups_per_split;
   if (gps == 0 && max_groups > 0) {
-    // One round of workgroups: as many splits per (sequence, kv-head) as fit on the
-    // device at once next to the FP16-window workgroups.
+    // As many split workgroups as fit on the device at once next to the FP16-window
+    // workgroups, each reading about the same number of groups, so a sequence gets
+    // splits in proportion to its length. With unequal lengths the splits are made
+    // three times finer, so that the last splits of the sequences even out.
     if (c->resident_blocks == 0)
       c->resident_blocks = std::max(1, kvq::decode_resident_blocks(c->cfg.bits,
                                                                    c->cfg.num_q_heads / c->cfg.num_kv_heads));
-    const int64_t bh = int64_t(c->cfg.batch) * c->cfg.num_kv_heads;
-    const int64_t win = bh * c->L.win_blocks;
-    const int64_t slots = std::max<int64_t>(bh, c->resident_blocks - std::min<int64_t>(win, c->resident_blocks / 4));
-    const int64_t splits = std::max<int64_t>(1, slots / bh);
-    gps = std::max<int64_t>(kvq::kMinGroupsPerSplit, (max_groups + splits - 1) / splits);
+    const int64_t win = int64_t(B) * Hkv * c->L.win_blocks;
+    const int64_t slots = std::max<int64_t>(int64_t(B) * Hkv,
+                                            c->resident_blocks - std::min<int64_t>(win, c->resident_blocks / 4));
+    const int64_t rounds = uniform_lengths ? 1 : 3;
+    gps = std::max<int64_t>(kvq::kMinGroupsPerSplit, (sum_groups * Hkv + slots * rounds - 1) / (slots * rounds));
   }
   if (gps == 0) gps = kvq::kMinGroupsPerSplit;
-  int64_t nsplit = max_groups == 0 ? 0 : (max_groups + gps - 1) / gps;
-  if (nsplit > c->L.max_splits) {
-    gps = (max_groups + c->L.max_splits - 1) / c->L.max_splits;
-    nsplit = (max_groups + gps - 1) / gps;
+  // Every sequence's split count must stay within the partial slots.
+  gps = std::max<int64_t>(gps, (max_groups + c->L.max_splits - 1) / c->L.max_splits);
+  kvq::SplitPlan plan{};
+  int64_t max_split = 0;
+  if (B <= kvq::kInlineSeqs) {
+    // Longest sequences first, so that their splits are dispatched first.
+    int order[kvq::kInlineSeqs];
+    for (int b = 0; b < B; b++) order[b] = b;
+    std::stable_sort(order, order + B, [&](int x, int y) { return c->Q[x] > c->Q[y]; });
+    plan.use_prefix = 1;
+    plan.prefix[0] = 0;
+    for (int p = 0; p < B; p++) {
+      const int b = order[p];
+      const int64_t n = (c->Q[b] / kvq::kGroup + gps - 1) / gps;
+      max_split = std::max(max_split, n);
+      plan.seq[p] = int16_t(b);
+      plan.count[b] = int16_t(n);
+      plan.prefix[p + 1] = plan.prefix[p] + int32_t(n);
+    }
+  } else {
+    plan.use_prefix = 0;
+    max_split = (max_groups + gps - 1) / gps;
+    plan.uniform = int32_t(max_split);
   }
+  plan.pstride = int32_t(max_split) + c->L.win_blocks;
   const float scale_log2 = c->cfg.softmax_scale * 1.4426950408889634f;
   const SeqDesc* dev_seq = reinterpret_cast<const SeqDesc*>(c->base + c->L.seq_off);
-  hipError_t e = kvq::launch_decode(c->L, c->base, dev_seq, q, out, int32_t(gps), int32_t(nsplit),
+  hipError_t e = kvq::launch_decode(c->L, c->base, dev_seq, q, out, int32_t(gps), plan,
                                     scale_log2, c->cfg.rotate, stream, c->prof_start, c->prof_stop);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode kernels failed: %s", hipGetErrorString(e));
   return ok();

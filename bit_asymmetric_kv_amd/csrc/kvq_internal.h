@@ -38,6 +38,21 @@ struct SeqArgs {
   int inl_valid;
 };
 
+// Decode work split: every kv-head of sequence b gets n_b split workgroups of
+// groups_per_split groups each. With use_prefix (batch at most kInlineSeqs) the
+// sequences are taken in the order seq[0], seq[1], ... (longest first) and
+// prefix[p] = n_seq[0] + ... + n_seq[p-1]; count[b] = n_b. Otherwise every sequence
+// has n_b = uniform, in index order. Partials of (sequence, query head) sit at
+// `pstride` slots: n_b splits, then the FP16 window's.
+struct SplitPlan {
+  int32_t prefix[kInlineSeqs + 1];
+  int16_t seq[kInlineSeqs];
+  int16_t count[kInlineSeqs];
+  int32_t use_prefix;
+  int32_t uniform;
+  int32_t pstride;
+};
+
 struct Layout {
   int32_t B, Hq, Hkv, bits, R, W;  // W = R + G ring slots
   int64_t gcap;                     // group blocks per (b, h)
@@ -57,11 +72,13 @@ hipError_t launch_ring_write(const Layout& L, uint8_t* base, const SeqArgs& seq,
 // Workgroups of the decode split kernel that fit on the current device at once.
 int decode_resident_blocks(int bits, int hg);
 hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* q,
-                         float* out, int32_t groups_per_split, int32_t nsplit, float scale_log2,
+                         float* out, int32_t groups_per_split, const SplitPlan& plan, float scale_log2,
                          int rotate, hipStream_t stream, hipEvent_t prof_start, hipEvent_t prof_stop);
 
-// Merge nparts partials per (sequence, query head) laid out [B][Hq][nparts][130].
-hipError_t launch_combine(const float* part, float* out, int Hq, int B, int nparts, hipStream_t stream);
+// Merge the partials of every (sequence, query head), laid out [B][Hq][pstride][130]:
+// sequence b has nsplit_b + wblocks of them (nsplit_b from the plan).
+hipError_t launch_combine(const float* part, float* out, int Hq, int B, const SplitPlan& plan, int wblocks,
+                          hipStream_t stream);
 
 // Comparison kernels: streaming read of a buffer; decode over a plain FP16 cache
 // [B][Hkv][t_cap][128] (partials [B][Hq][nsplit][130] in `part`).

@@ -152,3 +152,23 @@ def algorithmic_bytes(T: int, Q: int, bits: int, group: int = 32, head_dim: int 
     n_groups = Q // group
     per_group = 2 * group * head_dim * bits // 8 + 2 * (2 * head_dim) + 2 * (2 * group * head_dim // group)
     return n_groups * per_group + (T - Q) * 2 * 2 * head_dim
+
+
+def torch_key_params(torch, w: Workload, device):
+    """(multiplier, offset) of every kv-head's keys as device tensors [Hkv, D]."""
+    mult = np.stack([key_channel_params(w, h)[0] for h in range(w.num_kv_heads)])
+    off = np.stack([key_channel_params(w, h)[1] for h in range(w.num_kv_heads)])
+    return torch.tensor(mult, device=device), torch.tensor(off, device=device)
+
+
+def torch_kv(torch, w: Workload, params, n: int, gen, device):
+    """Seeded fp16 keys / values [B, n, Hkv, D] drawn on the device with the
+    workload's distribution (same rule as keys() / values(): k = m_d * (N(0,1) + mu_d),
+    v = N(0,1)), from torch's generator `gen`. For runs too large to draw on the
+    host; callers that check against the oracle copy the rows they check back."""
+    mult, off = params
+    shape = (w.batch, n, w.num_kv_heads, w.head_dim)
+    k = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    k = (mult * (k + off)).to(torch.float16)
+    v = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.float16)
+    return k.contiguous(), v.contiguous()

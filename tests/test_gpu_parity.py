@@ -65,6 +65,14 @@ def test_ragged_rotated_reduced(dev):
     _run(w, ctx, 36, dev, check_every=6)
 
 
+def test_batch_above_inline_records(dev):
+    # more sequences than fit in the kernels' by-value records: the per-sequence
+    # records go through the pinned upload path; ragged lengths, flushes interleaved
+    w = wl.WORKLOADS["ragged_b64_wht"].scaled(batch=72, num_q_heads=8, num_kv_heads=2, rotate=False, residual=32)
+    ctx = np.random.default_rng(9).integers(1, 260, size=72)
+    _run(w, ctx, 40, dev, check_every=10)
+
+
 @pytest.mark.parametrize("ratio", [1, 2, 4, 8])
 @pytest.mark.parametrize("bits", [2, 4])
 def test_gqa_ratios(dev, ratio, bits):
