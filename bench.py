@@ -2,7 +2,9 @@
 
 A step is one pass of the whole hot path: append one token per sequence (FP16
 window write, and a group quantize + pack whenever a group leaves the window),
-then decode attention over every cached token (split kernel + combine kernel).
+then decode attention over every cached token (split kernel + combine kernel),
+issued as one library call (kvq_decode_step; the window write happens inside the
+decode launch). The same step as two calls (append, then decode) is reported too.
 
 Workload (default): GQA layer, batch 1, 32 query / 8 KV heads, head_dim 128,
 context 131072, 2-bit, G = 32, R = 128. Several independent caches are built and
@@ -277,15 +279,16 @@ def main():
     dev = torch.device("cuda:0")
     w = wl.WORKLOADS[args.workload]
     total_steps = args.warmup + args.steps
-    max_tokens = int(w.context_lengths().max()) + total_steps + 1
+    max_tokens = int(w.context_lengths().max()) + total_steps + 64 + 1
     print(f"[bench] building {args.copies} caches of {w.name}", file=sys.stderr, flush=True)
     caches, params = build_caches(torch, kvq, w, args.copies, max_tokens, dev, args.groups_per_split)
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 7919)
-    knew, vnew = wl.torch_kv(torch, w, params, total_steps, gen, dev)   # [B, steps, Hkv, D]
-    knew = knew.transpose(0, 1).contiguous().view(total_steps, w.batch, 1, w.num_kv_heads, w.head_dim)
-    vnew = vnew.transpose(0, 1).contiguous().view(total_steps, w.batch, 1, w.num_kv_heads, w.head_dim)
+    knew, vnew = wl.torch_kv(torch, w, params, total_steps + 64, gen, dev)   # [B, steps, Hkv, D]
+    knew = knew.transpose(0, 1).contiguous().view(total_steps + 64, w.batch, 1, w.num_kv_heads, w.head_dim)
+    vnew = vnew.transpose(0, 1).contiguous().view(total_steps + 64, w.batch, 1, w.num_kv_heads, w.head_dim)
+    knew2, vnew2 = knew[total_steps:], vnew[total_steps:]
     q = torch.randn((total_steps, w.batch, w.num_q_heads, w.head_dim), generator=gen, device=dev).to(torch.float16)
     outs = [torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev) for _ in caches]
     torch.cuda.synchronize()
@@ -299,20 +302,31 @@ def main():
     t_start, t_end = ev.create(1)[0], ev.create(1)[0]
     for s in range(args.warmup):
         c = caches[s % len(caches)]
-        c.append(knew[s], vnew[s])
-        c.decode(q[s], outs[s % len(caches)])
+        c.step(knew[s], vnew[s], q[s], out=outs[s % len(caches)])
     torch.cuda.synchronize()
     ev.record(t_start, stream)
     host_t0 = time.perf_counter()
     for s in range(args.warmup, total_steps):
         c = caches[s % len(caches)]
-        c.append(knew[s], vnew[s])
-        c.decode(q[s], outs[s % len(caches)])
+        c.step(knew[s], vnew[s], q[s], out=outs[s % len(caches)])
         nbytes.append(step_bytes(c, w))
     host_enqueue_s = time.perf_counter() - host_t0
     ev.record(t_end, stream)
     torch.cuda.synchronize()
     total_ms = ev.elapsed_ms(t_start, t_end)
+
+    # The same step as two library calls (append, then decode), for reference.
+    n2 = min(args.steps, 64)
+    torch.cuda.synchronize()
+    ev.record(t_start, stream)
+    for i in range(n2):
+        s = total_steps + i
+        c = caches[s % len(caches)]
+        c.append(knew2[i], vnew2[i])
+        c.decode(q[i], outs[s % len(caches)])
+    ev.record(t_end, stream)
+    torch.cuda.synchronize()
+    two_call_us = ev.elapsed_ms(t_start, t_end) / n2 * 1e3
     bytes_avg = float(np.mean(nbytes))
     ms_per_step = total_ms / args.steps
     value = bytes_avg / (ms_per_step * 1e-3) / 1e9
@@ -395,6 +409,7 @@ def main():
                    "group": w.group, "residual": w.residual, "rotate": w.rotate,
                    "caches_round_robin": args.copies, "parallelism": "single GPU"},
         "step": {"algorithmic_bytes": int(bytes_avg), "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+                 "two_call_us_per_step": round(two_call_us, 2),
                  "decode_split_kernel_us": round(kern_avg_ms * 1e3, 2),
                  "decode_split_kernel_p10_p50_p90_us": [round(float(np.percentile(kern_ms, p)) * 1e3, 2)
                                                         for p in (10, 50, 90)],

@@ -30,7 +30,7 @@ KVQ_PART_RING_V = 2
 EXPORTED = (
     "kvq_cache_bytes", "kvq_create", "kvq_append", "kvq_decode_attention", "kvq_set_decode_split",
     "kvq_destroy", "kvq_seq_len", "kvq_group_bytes", "kvq_read_state", "kvq_last_error",
-    "kvq_set_profile_events", "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention",
+    "kvq_set_profile_events", "kvq_decode_step", "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention",
 )
 
 
@@ -83,6 +83,7 @@ def load() -> ctypes.CDLL:
     lib.kvq_create.argtypes = [cfgp, vp, sz, vp, ctypes.POINTER(vp)]
     lib.kvq_append.argtypes = [vp, vp, vp, ctypes.POINTER(i32), i32, vp]
     lib.kvq_decode_attention.argtypes = [vp, vp, vp, vp]
+    lib.kvq_decode_step.argtypes = [vp, vp, vp, ctypes.POINTER(i32), i32, vp, vp, vp]
     lib.kvq_set_decode_split.argtypes = [vp, i32]
     lib.kvq_set_profile_events.argtypes = [vp, vp, vp]
     lib.kvq_destroy.argtypes = [vp]
@@ -99,7 +100,7 @@ def load() -> ctypes.CDLL:
     lib.kvq_fp16_decode_attention.argtypes = [f16p, vp, vp, vp, i64, vp, vp, vp, sz, vp]
     for name in ("kvq_cache_bytes", "kvq_create", "kvq_append", "kvq_decode_attention",
                  "kvq_set_decode_split", "kvq_seq_len", "kvq_read_state", "kvq_set_profile_events",
-                 "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention"):
+                 "kvq_decode_step", "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -199,6 +200,31 @@ class KVCache:
         check(load().kvq_decode_attention(self._handle, ctypes.c_void_p(q.data_ptr()),
                                           ctypes.c_void_p(out.data_ptr()),
                                           ctypes.c_void_p(_stream_ptr(torch, self.device))))
+        return out
+
+    def step(self, k, v, q, n_tokens=None, out=None):
+        """Append k, v (fp16 [B, n_max, Hkv, D]; n_tokens per sequence or None) and
+        decode q (fp16 [B, Hq, D]) in one library call -> fp32 [B, Hq, D]."""
+        torch = self._torch
+        n_max = k.shape[1]
+        kshape = (self.cfg.batch, n_max, self.cfg.num_kv_heads, self.cfg.head_dim)
+        self._check_tensor(k, kshape, torch.float16, "k")
+        self._check_tensor(v, kshape, torch.float16, "v")
+        qshape = (self.cfg.batch, self.cfg.num_q_heads, self.cfg.head_dim)
+        self._check_tensor(q, qshape, torch.float16, "q")
+        if out is None:
+            out = torch.empty(qshape, dtype=torch.float32, device=self.device)
+        else:
+            self._check_tensor(out, qshape, torch.float32, "out")
+        arr = None
+        if n_tokens is not None:
+            vals = [int(x) for x in n_tokens]
+            if len(vals) != self.cfg.batch:
+                raise ValueError("n_tokens must have one entry per sequence")
+            arr = (ctypes.c_int32 * self.cfg.batch)(*vals)
+        check(load().kvq_decode_step(self._handle, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                     arr, n_max, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                     ctypes.c_void_p(_stream_ptr(torch, self.device))))
         return out
 
     def set_decode_split(self, groups_per_split: int):

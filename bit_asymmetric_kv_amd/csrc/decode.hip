@@ -40,8 +40,8 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 
 struct DecodeArgs {
   const uint8_t* blocks;
-  const __half* ringk;
-  const __half* ringv;
+  __half* ringk;  // written only by a folded append, for its new window tokens
+  __half* ringv;
   const SeqDesc* seq;
   const __half* q;
   float* part;
@@ -49,6 +49,7 @@ struct DecodeArgs {
   int B, Hkv, Hq, W, gps, rotate;
   int wblocks;  // FP16-window workgroups per (sequence, kv-head)
   SplitPlan plan;  // split workgroups per sequence and the partial slots per query head
+  AppendArgs app;  // an append folded into this launch (app.pending)
   float scale_log2;
 };
 
@@ -244,8 +245,10 @@ __device__ void merge_and_store(const DecodeArgs& a, int b, int h, int split, co
 // goes to its slot of `wp`. All loads of the chunk are issued first. Scores: lane l
 // takes token l % 32 and channel half l / 32. Weighted values: lane l accumulates
 // channels 2l and 2l + 1 over the chunk's tokens.
+// With an append folded into the launch (caches without rotation), tokens
+// t >= t_old come from the appended rows and are written to the ring.
 template <int HG>
-__device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt, const float (*qf)[kD],
+__device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt, int t_old, const float (*qf)[kD],
                              const float* expo, const WaveParts& wp, int wave, int lane) {
   if (cnt <= 0) {
     if (lane < HG) {
@@ -258,24 +261,46 @@ __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt,
   const int s0 = t0 % a.W;
   const int tl = lane % 32, hf = lane / 32;
   const bool kval = tl < cnt;
+  const bool pend = a.app.pending != 0;
+  const __half* kin = static_cast<const __half*>(a.app.k);
+  const __half* vin = static_cast<const __half*>(a.app.v);
+  // Appended token t of this (b, h): row (b, t - t_old, h) of k / v.
+  auto in_row = [&](int t) { return ((size_t(b) * a.app.n_max + (t - t_old)) * a.Hkv + h) * kD; };
+  const int tk = t0 + (kval ? tl : 0);
+  const bool knew = pend && tk >= t_old;
+  int kslot = s0 + (kval ? tl : 0);
+  if (kslot >= a.W) kslot -= a.W;
   uint4 kr[8];
   {
-    int slot = s0 + (kval ? tl : 0);
-    if (slot >= a.W) slot -= a.W;
-    const uint4* krow = reinterpret_cast<const uint4*>(a.ringk + (row0 + slot) * kD + 64 * hf);
+    const __half* src = knew ? kin + in_row(tk) : a.ringk + (row0 + kslot) * kD;
+    const uint4* krow = reinterpret_cast<const uint4*>(src + 64 * hf);
     for (int i = 0; i < 8; i++) kr[i] = krow[i];
   }
   uint32_t vr[kG];
   for (int t = 0; t < kG; t++) {
+    const int tt = t0 + (t < cnt ? t : 0);
     int slot = s0 + (t < cnt ? t : 0);
     if (slot >= a.W) slot -= a.W;
-    vr[t] = *reinterpret_cast<const uint32_t*>(a.ringv + (row0 + slot) * kD + 2 * lane);
+    const __half* src = pend && tt >= t_old ? vin + in_row(tt) : a.ringv + (row0 + slot) * kD;
+    vr[t] = *reinterpret_cast<const uint32_t*>(src + 2 * lane);
   }
 
   float kf[64];
   for (int i = 0; i < 8; i++) {
     const half8 k8 = __builtin_bit_cast(half8, kr[i]);
     for (int e = 0; e < 8; e++) kf[8 * i + e] = float(k8[e]);
+  }
+  if (pend && t0 + cnt > t_old) {
+    // Appended tokens in this chunk: write their keys and values to the ring.
+    if (knew && kval) {
+      uint4* dst = reinterpret_cast<uint4*>(a.ringk + (row0 + kslot) * kD + 64 * hf);
+      for (int i = 0; i < 8; i++) dst[i] = kr[i];
+    }
+    for (int t = max(0, t_old - t0); t < cnt; t++) {
+      int slot = s0 + t;
+      if (slot >= a.W) slot -= a.W;
+      *reinterpret_cast<uint32_t*>(a.ringv + (row0 + slot) * kD + 2 * lane) = vr[t];
+    }
   }
   float p[HG];
   for (int hh = 0; hh < HG; hh++) {
@@ -498,7 +523,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
   }
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const SeqDesc sd = a.seq[b];
+  const SeqDesc sd = (a.app.pending && a.app.seq.inl_valid) ? a.app.seq.inl[b] : a.seq[b];
   const int T = sd.t_old + sd.n_new, Q = sd.q_new;
   const int ng = Q / kG;
 
@@ -530,7 +555,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     // Window workgroup wsub takes chunks 4 * wsub + wave of the window [Q, T).
     const int chunk = (split - nsb) * kWaves + wave;
     const int t0 = Q + chunk * kG;
-    window_chunk<HG>(a, b, h, t0, min(kG, T - t0), qf, expo, wp, wave, lane);
+    window_chunk<HG>(a, b, h, t0, min(kG, T - t0), sd.t_old, qf, expo, wp, wave, lane);
+    // A folded append with inline records: store them as the sequence's state.
+    if (a.app.pending && a.app.seq.inl_valid && h == 0 && split == nsb && threadIdx.x == 0)
+      a.app.seq.state[b] = sd;
     merge_and_store<HG>(a, b, h, split, wp);
     return;
   }
@@ -794,14 +822,14 @@ int decode_resident_blocks(int bits, int hg) {
          : hg == 4 ? resident_blocks_of<4, 4>() : resident_blocks_of<4, 8>();
 }
 
-hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* q, float* out,
-                         int32_t groups_per_split, const SplitPlan& plan, float scale_log2, int rotate,
+hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const AppendArgs& app, const void* q,
+                         float* out, int32_t groups_per_split, const SplitPlan& plan, float scale_log2, int rotate,
                          hipStream_t stream,
                          hipEvent_t prof_start, hipEvent_t prof_stop) {
   DecodeArgs a;
   a.blocks = base + L.blocks_off;
-  a.ringk = reinterpret_cast<const __half*>(base + L.ringk_off);
-  a.ringv = reinterpret_cast<const __half*>(base + L.ringv_off);
+  a.ringk = reinterpret_cast<__half*>(base + L.ringk_off);
+  a.ringv = reinterpret_cast<__half*>(base + L.ringv_off);
   a.seq = seq;
   a.q = static_cast<const __half*>(q);
   a.part = reinterpret_cast<float*>(base + L.part_off);
@@ -811,6 +839,7 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   a.W = L.W;
   a.gps = groups_per_split;
   a.plan = plan;
+  a.app = app;
   a.wblocks = L.win_blocks;
   a.B = L.B;
   a.rotate = rotate;

@@ -232,12 +232,26 @@ kvq_status kvq_set_profile_events(kvq_cache* c, hipEvent_t start, hipEvent_t sto
   return ok();
 }
 
-kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, const int32_t* n_tokens,
-                      int32_t n_max, hipStream_t stream) {
-  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+}  // extern "C"
+
+namespace {
+
+// An append that has been checked and described but not yet launched.
+struct PendingAppend {
+  kvq::SeqArgs sa;
+  std::vector<int64_t> T2, Q2;  // lengths after the append
+  int32_t max_flush = 0;        // groups leaving the window, most of any sequence
+  int32_t max_ring = 0;         // appended tokens staying in the window, most of any sequence
+  int64_t total_new = 0;
+};
+
+// Checks an append and fills its per-sequence records (inline for small batches,
+// otherwise uploaded on `stream` from pinned staging into the device state).
+kvq_status prepare_append(kvq_cache* c, const void* k, const void* v, const int32_t* n_tokens, int32_t n_max,
+                          hipStream_t stream, PendingAppend& pa) {
   const int B = c->cfg.batch;
   if (n_max < 0) return fail(KVQ_ERR_INVALID_ARG, "n_max must be >= 0");
-  int64_t total_new = 0;
+  pa.total_new = 0;
   for (int b = 0; b < B; b++) {
     int64_t n = n_tokens ? n_tokens[b] : n_max;
     if (n < 0 || n > n_max)
@@ -245,17 +259,16 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, const int32_t*
     if (c->T[b] + n > c->cfg.max_tokens)
       return fail(KVQ_ERR_CAPACITY, "sequence %d would hold %lld tokens > max_tokens %lld", b,
                   (long long)(c->T[b] + n), (long long)c->cfg.max_tokens);
-    total_new += n;
+    pa.total_new += n;
   }
-  if (total_new == 0) return ok();
+  pa.T2 = c->T;
+  pa.Q2 = c->Q;
+  if (pa.total_new == 0) return ok();
   if (!k || !v) return fail(KVQ_ERR_INVALID_ARG, "k and v must be device pointers when tokens are appended");
 
   // Host bookkeeping: new lengths, groups leaving the window, tokens entering it.
-  // Small batches pass the per-sequence records to the kernels by value; larger ones
-  // upload them from a pinned staging buffer.
   const bool inl = B <= kvq::kInlineSeqs;
-  kvq::SeqArgs sa;
-  SeqDesc* d = sa.inl;
+  SeqDesc* d = pa.sa.inl;
   int slot = -1;
   if (!inl) {
     slot = c->next_staging;
@@ -264,100 +277,94 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, const int32_t*
       return fail(KVQ_ERR_HIP, "waiting for a staging buffer failed: %s", hipGetErrorString(hipGetLastError()));
     d = c->staging[slot];
   }
-  int32_t max_flush = 0, max_ring = 0;
-  std::vector<int64_t> T2(B), Q2(B);
+  pa.max_flush = pa.max_ring = 0;
   for (int b = 0; b < B; b++) {
     int64_t n = n_tokens ? n_tokens[b] : n_max;
-    T2[b] = c->T[b] + n;
-    Q2[b] = quantized_count(T2[b], c->cfg.residual);
+    pa.T2[b] = c->T[b] + n;
+    pa.Q2[b] = quantized_count(pa.T2[b], c->cfg.residual);
     d[b].t_old = int32_t(c->T[b]);
     d[b].n_new = int32_t(n);
     d[b].q_old = int32_t(c->Q[b]);
-    d[b].q_new = int32_t(Q2[b]);
-    max_flush = std::max<int32_t>(max_flush, int32_t((Q2[b] - c->Q[b]) / kvq::kGroup));
+    d[b].q_new = int32_t(pa.Q2[b]);
+    pa.max_flush = std::max<int32_t>(pa.max_flush, int32_t((pa.Q2[b] - c->Q[b]) / kvq::kGroup));
     // appended tokens that stay in the FP16 window
-    int64_t first_kept = std::max<int64_t>(c->T[b], Q2[b]);
-    max_ring = std::max<int32_t>(max_ring, int32_t(std::max<int64_t>(0, T2[b] - first_kept)));
+    int64_t first_kept = std::max<int64_t>(c->T[b], pa.Q2[b]);
+    pa.max_ring = std::max<int32_t>(pa.max_ring, int32_t(std::max<int64_t>(0, pa.T2[b] - first_kept)));
   }
   SeqDesc* dev_seq = reinterpret_cast<SeqDesc*>(c->base + c->L.seq_off);
-  sa.dev = dev_seq;
-  sa.state = dev_seq;
-  sa.inl_valid = inl ? 1 : 0;
+  pa.sa.dev = dev_seq;
+  pa.sa.state = dev_seq;
+  pa.sa.inl_valid = inl ? 1 : 0;
   if (!inl && (hipMemcpyAsync(dev_seq, d, sizeof(SeqDesc) * B, hipMemcpyHostToDevice, stream) != hipSuccess ||
                hipEventRecord(c->staging_done[slot], stream) != hipSuccess))
     return fail(KVQ_ERR_HIP, "uploading sequence state failed: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+// Decode over lengths T, Q (the host mirror after any append in the same call);
+// with `pa`, the decode kernel also writes that append's tokens into the window.
+kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const std::vector<int64_t>& Q,
+                             const PendingAppend* pa, const void* k, const void* v, int32_t n_max, const void* q,
+                             float* out, hipStream_t stream);
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, const int32_t* n_tokens,
+                      int32_t n_max, hipStream_t stream) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  PendingAppend pa;
+  kvq_status st = prepare_append(c, k, v, n_tokens, n_max, stream, pa);
+  if (st != KVQ_OK || pa.total_new == 0) return st;
   hipError_t e = hipSuccess;
-  if (max_flush > 0)
-    e = kvq::launch_flush(c->L, c->base, sa, k, v, n_max, max_flush, c->cfg.rotate, stream);
+  if (pa.max_flush > 0)
+    e = kvq::launch_flush(c->L, c->base, pa.sa, k, v, n_max, pa.max_flush, c->cfg.rotate, stream);
   // The window-write kernel always runs: with inline records it also stores them.
-  if (e == hipSuccess && (max_ring > 0 || inl))
-    e = kvq::launch_ring_write(c->L, c->base, sa, k, v, n_max, std::max(max_ring, 1), c->cfg.rotate, stream);
+  if (e == hipSuccess && (pa.max_ring > 0 || pa.sa.inl_valid))
+    e = kvq::launch_ring_write(c->L, c->base, pa.sa, k, v, n_max, std::max(pa.max_ring, 1), c->cfg.rotate, stream);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append kernels failed: %s", hipGetErrorString(e));
-  c->T = T2;
-  c->Q = Q2;
+  c->T = pa.T2;
+  c->Q = pa.Q2;
+  return ok();
+}
+
+kvq_status kvq_decode_step(kvq_cache* c, const void* k, const void* v, const int32_t* n_tokens, int32_t n_max,
+                           const void* q, float* out, hipStream_t stream) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q and out must be device pointers");
+  PendingAppend pa;
+  // Checks that need no launch come first, so that a failing call changes nothing.
+  {
+    const int B = c->cfg.batch;
+    if (n_max < 0) return fail(KVQ_ERR_INVALID_ARG, "n_max must be >= 0");
+    for (int b = 0; b < B; b++) {
+      const int64_t n = n_tokens ? n_tokens[b] : n_max;
+      if (n >= 0 && n <= n_max && c->T[b] + n == 0) return fail(KVQ_ERR_EMPTY, "sequence %d holds no token", b);
+    }
+  }
+  kvq_status st = prepare_append(c, k, v, n_tokens, n_max, stream, pa);
+  if (st != KVQ_OK) return st;
+  // Rotated caches keep the separate window-write kernel (it rotates the new keys);
+  // otherwise the decode launch writes the new window tokens itself.
+  const bool fold = pa.total_new > 0 && !c->cfg.rotate;
+  hipError_t e = hipSuccess;
+  if (pa.total_new > 0 && pa.max_flush > 0)
+    e = kvq::launch_flush(c->L, c->base, pa.sa, k, v, n_max, pa.max_flush, c->cfg.rotate, stream);
+  if (e == hipSuccess && pa.total_new > 0 && !fold && (pa.max_ring > 0 || pa.sa.inl_valid))
+    e = kvq::launch_ring_write(c->L, c->base, pa.sa, k, v, n_max, std::max(pa.max_ring, 1), c->cfg.rotate, stream);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append kernels failed: %s", hipGetErrorString(e));
+  st = launch_decode_for(c, pa.T2, pa.Q2, fold ? &pa : nullptr, k, v, n_max, q, out, stream);
+  if (st != KVQ_OK) return st;
+  c->T = pa.T2;
+  c->Q = pa.Q2;
   return ok();
 }
 
 kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, hipStream_t stream) {
   if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
   if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q and out must be device pointers");
-  const int B = c->cfg.batch, Hkv = c->cfg.num_kv_heads;
-  int64_t max_groups = 0, sum_groups = 0;
-  for (int b = 0; b < B; b++) {
-    if (c->T[b] == 0) return fail(KVQ_ERR_EMPTY, "sequence %d holds no token", b);
-    max_groups = std::max(max_groups, c->Q[b] / kvq::kGroup);
-    sum_groups += c->Q[b] / kvq::kGroup;
-  }
-  // Equal lengths: one round of equal workgroups. Unequal lengths: about three
-  // rounds of smaller ones, longest sequences first.
-  const bool uniform_lengths = sum_groups == max_groups * B;
-  int64_t gps = c->groups_per_split;
-  if (gps == 0 && max_groups > 0) {
-    // As many split workgroups as fit on the device at once next to the FP16-window
-    // workgroups, each reading about the same number of groups, so a sequence gets
-    // splits in proportion to its length. With unequal lengths the splits are made
-    // three times finer, so that the last splits of the sequences even out.
-    if (c->resident_blocks == 0)
-      c->resident_blocks = std::max(1, kvq::decode_resident_blocks(c->cfg.bits,
-                                                                   c->cfg.num_q_heads / c->cfg.num_kv_heads));
-    const int64_t win = int64_t(B) * Hkv * c->L.win_blocks;
-    const int64_t slots = std::max<int64_t>(int64_t(B) * Hkv,
-                                            c->resident_blocks - std::min<int64_t>(win, c->resident_blocks / 4));
-    const int64_t rounds = uniform_lengths ? 1 : 3;
-    gps = std::max<int64_t>(kvq::kMinGroupsPerSplit, (sum_groups * Hkv + slots * rounds - 1) / (slots * rounds));
-  }
-  if (gps == 0) gps = kvq::kMinGroupsPerSplit;
-  // Every sequence's split count must stay within the partial slots.
-  gps = std::max<int64_t>(gps, (max_groups + c->L.max_splits - 1) / c->L.max_splits);
-  kvq::SplitPlan plan{};
-  int64_t max_split = 0;
-  if (B <= kvq::kInlineSeqs) {
-    // Longest sequences first, so that their splits are dispatched first.
-    int order[kvq::kInlineSeqs];
-    for (int b = 0; b < B; b++) order[b] = b;
-    std::stable_sort(order, order + B, [&](int x, int y) { return c->Q[x] > c->Q[y]; });
-    plan.use_prefix = 1;
-    plan.prefix[0] = 0;
-    for (int p = 0; p < B; p++) {
-      const int b = order[p];
-      const int64_t n = (c->Q[b] / kvq::kGroup + gps - 1) / gps;
-      max_split = std::max(max_split, n);
-      plan.seq[p] = int16_t(b);
-      plan.count[b] = int16_t(n);
-      plan.prefix[p + 1] = plan.prefix[p] + int32_t(n);
-    }
-  } else {
-    plan.use_prefix = 0;
-    max_split = (max_groups + gps - 1) / gps;
-    plan.uniform = int32_t(max_split);
-  }
-  plan.pstride = int32_t(max_split) + c->L.win_blocks;
-  const float scale_log2 = c->cfg.softmax_scale * 1.4426950408889634f;
-  const SeqDesc* dev_seq = reinterpret_cast<const SeqDesc*>(c->base + c->L.seq_off);
-  hipError_t e = kvq::launch_decode(c->L, c->base, dev_seq, q, out, int32_t(gps), plan,
-                                    scale_log2, c->cfg.rotate, stream, c->prof_start, c->prof_stop);
-  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode kernels failed: %s", hipGetErrorString(e));
-  return ok();
+  return launch_decode_for(c, c->T, c->Q, nullptr, nullptr, nullptr, 0, q, out, stream);
 }
 
 kvq_status kvq_read_state(kvq_cache* c, int32_t part, int32_t b, int32_t h, size_t offset,
@@ -466,3 +473,77 @@ kvq_status kvq_fp16_decode_attention(const kvq_fp16_config* cfg, const void* k, 
 }
 
 }  // extern "C"
+
+namespace {
+
+kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const std::vector<int64_t>& Q,
+                             const PendingAppend* pa, const void* k, const void* v, int32_t n_max, const void* q,
+                             float* out, hipStream_t stream) {
+  const int B = c->cfg.batch, Hkv = c->cfg.num_kv_heads;
+  int64_t max_groups = 0, sum_groups = 0;
+  for (int b = 0; b < B; b++) {
+    if (T[b] == 0) return fail(KVQ_ERR_EMPTY, "sequence %d holds no token", b);
+    max_groups = std::max(max_groups, Q[b] / kvq::kGroup);
+    sum_groups += Q[b] / kvq::kGroup;
+  }
+  // Equal lengths: one round of equal workgroups. Unequal lengths: about three
+  // rounds of smaller ones, longest sequences first.
+  const bool uniform_lengths = sum_groups == max_groups * B;
+  int64_t gps = c->groups_per_split;
+  if (gps == 0 && max_groups > 0) {
+    // As many split workgroups as fit on the device at once next to the FP16-window
+    // workgroups, each reading about the same number of groups, so a sequence gets
+    // splits in proportion to its length. With unequal lengths the splits are made
+    // three times finer, so that the last splits of the sequences even out.
+    if (c->resident_blocks == 0)
+      c->resident_blocks = std::max(1, kvq::decode_resident_blocks(c->cfg.bits,
+                                                                   c->cfg.num_q_heads / c->cfg.num_kv_heads));
+    const int64_t win = int64_t(B) * Hkv * c->L.win_blocks;
+    const int64_t slots = std::max<int64_t>(int64_t(B) * Hkv,
+                                            c->resident_blocks - std::min<int64_t>(win, c->resident_blocks / 4));
+    const int64_t rounds = uniform_lengths ? 1 : 3;
+    gps = std::max<int64_t>(kvq::kMinGroupsPerSplit, (sum_groups * Hkv + slots * rounds - 1) / (slots * rounds));
+  }
+  if (gps == 0) gps = kvq::kMinGroupsPerSplit;
+  // Every sequence's split count must stay within the partial slots.
+  gps = std::max<int64_t>(gps, (max_groups + c->L.max_splits - 1) / c->L.max_splits);
+  kvq::SplitPlan plan{};
+  int64_t max_split = 0;
+  if (B <= kvq::kInlineSeqs) {
+    // Longest sequences first, so that their splits are dispatched first.
+    int order[kvq::kInlineSeqs];
+    for (int b = 0; b < B; b++) order[b] = b;
+    std::stable_sort(order, order + B, [&](int x, int y) { return Q[x] > Q[y]; });
+    plan.use_prefix = 1;
+    plan.prefix[0] = 0;
+    for (int p = 0; p < B; p++) {
+      const int b = order[p];
+      const int64_t n = (Q[b] / kvq::kGroup + gps - 1) / gps;
+      max_split = std::max(max_split, n);
+      plan.seq[p] = int16_t(b);
+      plan.count[b] = int16_t(n);
+      plan.prefix[p + 1] = plan.prefix[p] + int32_t(n);
+    }
+  } else {
+    plan.use_prefix = 0;
+    max_split = (max_groups + gps - 1) / gps;
+    plan.uniform = int32_t(max_split);
+  }
+  plan.pstride = int32_t(max_split) + c->L.win_blocks;
+  const float scale_log2 = c->cfg.softmax_scale * 1.4426950408889634f;
+  const SeqDesc* dev_seq = reinterpret_cast<const SeqDesc*>(c->base + c->L.seq_off);
+  kvq::AppendArgs app{};
+  if (pa) {
+    app.pending = 1;
+    app.k = k;
+    app.v = v;
+    app.n_max = n_max;
+    app.seq = pa->sa;
+  }
+  hipError_t e = kvq::launch_decode(c->L, c->base, dev_seq, app, q, out, int32_t(gps), plan,
+                                    scale_log2, c->cfg.rotate, stream, c->prof_start, c->prof_stop);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode kernels failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace

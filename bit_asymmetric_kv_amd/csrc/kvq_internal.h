@@ -38,6 +38,19 @@ struct SeqArgs {
   int inl_valid;
 };
 
+// An append folded into a decode launch (caches without rotation): the FP16-window
+// workgroups read the appended tokens from k / v ([B][n_max][Hkv][128] fp16), write
+// the tokens that stay in the window to the ring, and with inline records store them
+// as the sequences' state. Every workgroup takes the sequence lengths from `seq`
+// (inline) or the device state (uploaded records).
+struct AppendArgs {
+  int32_t pending;
+  const void* k;
+  const void* v;
+  int32_t n_max;
+  SeqArgs seq;
+};
+
 // Decode work split: every kv-head of sequence b gets n_b split workgroups of
 // groups_per_split groups each. With use_prefix (batch at most kInlineSeqs) the
 // sequences are taken in the order seq[0], seq[1], ... (longest first) and
@@ -71,9 +84,10 @@ hipError_t launch_ring_write(const Layout& L, uint8_t* base, const SeqArgs& seq,
                              hipStream_t stream);
 // Workgroups of the decode split kernel that fit on the current device at once.
 int decode_resident_blocks(int bits, int hg);
-hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const void* q,
-                         float* out, int32_t groups_per_split, const SplitPlan& plan, float scale_log2,
-                         int rotate, hipStream_t stream, hipEvent_t prof_start, hipEvent_t prof_stop);
+hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const AppendArgs& app,
+                         const void* q, float* out, int32_t groups_per_split, const SplitPlan& plan,
+                         float scale_log2, int rotate, hipStream_t stream, hipEvent_t prof_start,
+                         hipEvent_t prof_stop);
 
 // Merge the partials of every (sequence, query head), laid out [B][Hq][pstride][130]:
 // sequence b has nsplit_b + wblocks of them (nsplit_b from the plan).

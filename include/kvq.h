@@ -110,6 +110,16 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v,
  * Errors: KVQ_ERR_EMPTY if any sequence holds no token. */
 kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, hipStream_t stream);
 
+/* One decode step in one call: exactly kvq_append(c, k, v, n_tokens, n_max)
+ * followed by kvq_decode_attention(c, q, out), with the same arguments, results
+ * and errors (KVQ_ERR_EMPTY is checked after counting the appended tokens; on any
+ * error nothing is appended). For caches without rotation the decode launch itself
+ * writes the appended tokens that stay in the FP16 window (their rows are read from
+ * k / v), so a step costs the decode kernels plus, once per G tokens, the group
+ * flush; rotated caches run the separate window-write kernel first. */
+kvq_status kvq_decode_step(kvq_cache* c, const void* k, const void* v, const int32_t* n_tokens, int32_t n_max,
+                           const void* q, float* out, hipStream_t stream);
+
 /* Override the number of 32-token groups one workgroup of the decode kernel
  * reads (0 restores the automatic choice). Must be 0 or in [4, 1 << 20]. */
 kvq_status kvq_set_decode_split(kvq_cache* c, int32_t groups_per_split);
