@@ -12,8 +12,9 @@
 // window; each writes partial (max, sum, unnormalized output) per query head, and a
 // second kernel merges them.
 //
-// Inside a split each wave streams whole 32-token groups. Every group block is read
-// from HBM once and serves all query heads of the kv-head:
+// Inside a split each wave streams whole 32-token groups straight into registers,
+// two groups ahead of the one it computes on. Every group block is read from HBM
+// once and serves all query heads of the kv-head:
 //  * scores: an MFMA 16x16x32 f16 contraction over channels with the key codes as
 //    A (converted exactly to f16 by the scaled fp4/fp8 conversions) and, as B, the
 //    query multiplied by the group's per-channel key scale, split into fp16 high and
@@ -337,124 +338,13 @@ __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt,
   }
 }
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of this
-// wave are outstanding (expcnt and lgkmcnt left unconstrained).
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-template <int LPG, int NBUF>
-__device__ __forceinline__ void wait_group_loads(int outstanding_groups) {
-  // outstanding_groups is in [0, NBUF - 2]; each group is LPG load instructions.
-  if (outstanding_groups <= 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  else if (NBUF > 2 && outstanding_groups == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPG));
-  else if (NBUF > 3 && outstanding_groups == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPG));
-  else __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF > 4 ? 3 : 0) * LPG));
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// The bytes of one group block that a lane uses, read from the wave's shared-memory
-// copy of the block.
+// The bytes of one group block that a lane uses.
 template <int BITS, int NJ>
 struct GroupRegs {
   uint4 kc0, kc1, vc0, vc1;  // key / value code words (kc1, vc1 used at 4 bits)
   half8 ks, kz;              // key scale / zero of this lane's 8-channel block
   half8 vs[NJ], vz[NJ];      // value scale / zero of this lane's 8 tokens per channel group
 };
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
-
-// Byte offset of a shared-memory object inside the workgroup's LDS allocation.
-__device__ inline uint32_t lds_offset(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cu8*)p));
-}
-
-// The reads of a group block are written as one asm block that also waits for
-// them. The block's bytes arrive through direct HBM->LDS loads whose completion the
-// loop tracks itself with vmcnt (at most one later group still in flight); a
-// compiler-generated LDS read of the same array would instead be preceded by a wait
-// for every outstanding direct load, which drains the prefetch ring at every group.
-// Addresses: a0 = block + 16 * lane (code words), a1 = block + 16 * cb (key scale /
-// zero), a2 = block + 16 * (4 * kb + jbase) (value scale / zero).
-template <int BITS, int NJ>
-__device__ __forceinline__ void read_group(GroupRegs<BITS, NJ>& G, const uint8_t* blk, int lane, int cb, int kb,
-                                           int jbase) {
-  const uint32_t base = lds_offset(blk);
-  const uint32_t a0 = base + 16 * lane, a1 = base + 16 * cb, a2 = base + 16 * (kb * 4 + jbase);
-  u32x4 kc0, kc1, vc0, vc1, ks, kz, vs0, vz0, vs1, vz1;
-  if constexpr (BITS == 2 && NJ == 1) {
-    asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %6 offset:1024\n\t"
-        "ds_read_b128 %2, %7 offset:2048\n\t"
-        "ds_read_b128 %3, %7 offset:2304\n\t"
-        "ds_read_b128 %4, %8 offset:2560\n\t"
-        "ds_read_b128 %5, %8 offset:2816\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(kc0), "=&v"(vc0), "=&v"(ks), "=&v"(kz), "=&v"(vs0), "=&v"(vz0)
-        : "v"(a0), "v"(a1), "v"(a2)
-        : "memory");
-  } else if constexpr (BITS == 2 && NJ == 2) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:1024\n\t"
-        "ds_read_b128 %2, %9 offset:2048\n\t"
-        "ds_read_b128 %3, %9 offset:2304\n\t"
-        "ds_read_b128 %4, %10 offset:2560\n\t"
-        "ds_read_b128 %5, %10 offset:2816\n\t"
-        "ds_read_b128 %6, %10 offset:2576\n\t"
-        "ds_read_b128 %7, %10 offset:2832\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(kc0), "=&v"(vc0), "=&v"(ks), "=&v"(kz), "=&v"(vs0), "=&v"(vz0), "=&v"(vs1), "=&v"(vz1)
-        : "v"(a0), "v"(a1), "v"(a2)
-        : "memory");
-  } else if constexpr (BITS == 4 && NJ == 1) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:1024\n\t"
-        "ds_read_b128 %2, %8 offset:2048\n\t"
-        "ds_read_b128 %3, %8 offset:3072\n\t"
-        "ds_read_b128 %4, %9 offset:4096\n\t"
-        "ds_read_b128 %5, %9 offset:4352\n\t"
-        "ds_read_b128 %6, %10 offset:4608\n\t"
-        "ds_read_b128 %7, %10 offset:4864\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(kc0), "=&v"(kc1), "=&v"(vc0), "=&v"(vc1), "=&v"(ks), "=&v"(kz), "=&v"(vs0), "=&v"(vz0)
-        : "v"(a0), "v"(a1), "v"(a2)
-        : "memory");
-  } else {
-    static_assert(BITS == 4 && NJ == 2, "group block read: unsupported configuration");
-    asm volatile(
-        "ds_read_b128 %0, %10\n\t"
-        "ds_read_b128 %1, %10 offset:1024\n\t"
-        "ds_read_b128 %2, %10 offset:2048\n\t"
-        "ds_read_b128 %3, %10 offset:3072\n\t"
-        "ds_read_b128 %4, %11 offset:4096\n\t"
-        "ds_read_b128 %5, %11 offset:4352\n\t"
-        "ds_read_b128 %6, %12 offset:4608\n\t"
-        "ds_read_b128 %7, %12 offset:4864\n\t"
-        "ds_read_b128 %8, %12 offset:4624\n\t"
-        "ds_read_b128 %9, %12 offset:4880\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(kc0), "=&v"(kc1), "=&v"(vc0), "=&v"(vc1), "=&v"(ks), "=&v"(kz), "=&v"(vs0), "=&v"(vz0),
-          "=&v"(vs1), "=&v"(vz1)
-        : "v"(a0), "v"(a1), "v"(a2)
-        : "memory");
-  }
-  G.kc0 = __builtin_bit_cast(uint4, kc0);
-  G.vc0 = __builtin_bit_cast(uint4, vc0);
-  if constexpr (BITS == 4) {
-    G.kc1 = __builtin_bit_cast(uint4, kc1);
-    G.vc1 = __builtin_bit_cast(uint4, vc1);
-  }
-  G.ks = __builtin_bit_cast(half8, ks);
-  G.kz = __builtin_bit_cast(half8, kz);
-  G.vs[0] = __builtin_bit_cast(half8, vs0);
-  G.vz[0] = __builtin_bit_cast(half8, vz0);
-  if constexpr (NJ == 2) {
-    G.vs[1] = __builtin_bit_cast(half8, vs1);
-    G.vz[1] = __builtin_bit_cast(half8, vz1);
-  }
-}
 
 template <int BITS, int HG>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
@@ -468,13 +358,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int NCOPY = 16 / HG;                // columns per head
   constexpr int NJ = NCOPY >= 4 ? 1 : 4 / NCOPY;  // value channel groups handled per lane
   constexpr int GB = 2 * (kG * kD * BITS / 8) + 1024;
-  constexpr int LPG = GB / 1024;              // 16-byte-per-lane loads per group block
-  constexpr int NBUF = 2;                     // group blocks per wave in shared memory
   constexpr int ITEMS = (HG + 3) / 4;         // key-side operand items per lane
 
-  // Each wave streams its group blocks HBM -> shared memory with direct loads into a
-  // ring of NBUF blocks; after the loop the same bytes hold the wave's partial.
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][NBUF * GB];
+  __shared__ float wpart_mem[kWaves * HG * kPartialStride];  // per-wave partials
   __shared__ float qf[HG][kD];
   __shared__ float expo[HG];
   __shared__ union {
@@ -484,8 +370,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       half8 b[4][4][U];
     } bk[kWaves];
   } sh;
-  static_assert(NBUF * GB >= HG * kPartialStride * 4, "wave partial must fit in the wave's ring");
-  const WaveParts wp{reinterpret_cast<float*>(&ring[0][0]), NBUF * GB / 4};
+  const WaveParts wp{wpart_mem, HG * kPartialStride};
 
   // 1-D grid: the split workgroups first, sequence by sequence in the plan's order
   // (each sequence's n_b splits for each kv-head), then wblocks FP16-window
@@ -538,15 +423,26 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int n = __builtin_amdgcn_readfirstlane(tail ? 0 : max(0, wg1 - wg0));
 
   const uint8_t* base = a.blocks + (size_t(b) * a.Hkv + h) * size_t(a.gcap) * GB;
-  uint8_t* myring = &ring[wave][0];
-  auto issue = [&](int r) {  // group wg0 + r into ring slot r % NBUF
-    const uint8_t* src = base + size_t(wg0 + r) * GB + 16 * lane;
-    uint8_t* dst = myring + (r % NBUF) * GB;
-    for (int i = 0; i < LPG; i++) __builtin_amdgcn_global_load_lds(src + 1024 * i, dst + 1024 * i, 16, 0, 0);
+  // Group r's bytes of this lane, loaded straight into registers.
+  auto load_group = [&](int r, GroupRegs<BITS, NJ>& G) {
+    const uint8_t* blk = base + size_t(wg0 + r) * GB;
+    constexpr int CB = kG * kD * BITS / 8;
+    G.kc0 = *reinterpret_cast<const uint4*>(blk + 16 * lane);
+    G.vc0 = *reinterpret_cast<const uint4*>(blk + CB + 16 * lane);
+    if constexpr (BITS == 4) {
+      G.kc1 = *reinterpret_cast<const uint4*>(blk + 1024 + 16 * lane);
+      G.vc1 = *reinterpret_cast<const uint4*>(blk + CB + 1024 + 16 * lane);
+    }
+    G.ks = load_half8(blk + 2 * CB + 16 * (lane / 4));
+    G.kz = load_half8(blk + 2 * CB + 256 + 16 * (lane / 4));
+    const int kb_ = lane / 16, col_ = lane % 16, u_ = col_ % (2 * HG);
+    const int kcopy_ = 2 * (col_ / (2 * HG)) + (u_ < HG ? 0 : 1);
+    const int jbase_ = (kcopy_ % (4 / NJ)) * NJ;
+    for (int jr = 0; jr < NJ; jr++) {
+      G.vs[jr] = load_half8(blk + 2 * CB + 512 + 16 * (kb_ * 4 + jbase_ + jr));
+      G.vz[jr] = load_half8(blk + 2 * CB + 768 + 16 * (kb_ * 4 + jbase_ + jr));
+    }
   };
-  // Start streaming before the query preparation so that the two overlap.
-  for (int r = 0; r < NBUF - 1 && r < n; r++) issue(r);
-
   // The FP16-window workgroup and rotated queries use the shared-memory query
   // preparation; otherwise each wave prepares what its lanes need on its own.
   if (tail || a.rotate) prepare_query<HG>(a, b, h, qf, expo);
@@ -619,8 +515,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   for (int jr = 0; jr < NJ; jr++) zacc[jr] = 0.0f;
 
   // The group loop is software-pipelined: while group r's softmax and value side run,
-  // group r+1's bytes are read from shared memory and its key-side scores computed,
-  // so the two dependency chains overlap.
+  // group r+1's key-side scores are computed (its bytes are already in registers)
+  // and group r+2's bytes are on their way, so the dependency chains overlap.
   GroupRegs<BITS, NJ> G;   // group whose scores are in s0 / s1
   float4v s0, s1;
 
@@ -704,33 +600,26 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
+  GroupRegs<BITS, NJ> Gn, Gnn;
   if (n > 0) {
-    // Group r has landed once at most min(NBUF - 2, n - 1 - r) later groups are still
-    // in flight; after reading it, the slot read one iteration earlier is refilled.
-    wait_group_loads<LPG, NBUF>(min(NBUF - 2, n - 1));
-    read_group<BITS, NJ>(G, myring, lane, cb, kb, jbase);
-    if (NBUF - 1 < n) issue(NBUF - 1);
+    load_group(0, G);
+    if (n > 1) load_group(1, Gn);
     key_mfma(G, key_prep(G), s0, s1);
   }
   for (int r = 0; r + 1 < n; r++) {
-    GroupRegs<BITS, NJ> Gn;
-    wait_group_loads<LPG, NBUF>(min(NBUF - 2, n - 2 - r));
-    read_group<BITS, NJ>(Gn, myring + ((r + 1) % NBUF) * GB, lane, cb, kb, jbase);
-    if (r + NBUF < n) issue(r + NBUF);
+    if (r + 2 < n) load_group(r + 2, Gnn);
     const float qzn = key_prep(Gn);
     value_side(G, s0, s1);
     key_mfma(Gn, qzn, s0, s1);
     G = Gn;
+    Gn = Gnn;
   }
   if (n > 0) value_side(G, s0, s1);
 
-  // Wave partial: sums over the four row blocks, written over this wave's ring (all
-  // of its loads have completed).
+  // Wave partial: sums over the four row blocks.
   const float l_tot = wave_sum_rows(l_run);
   float zs[NJ];
   for (int jr = 0; jr < NJ; jr++) zs[jr] = wave_sum_rows(zacc[jr]);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   if (kb == 0 && kcopy == 0) {
     wp.at(wave, hd, 0) = m_run == -INFINITY ? -INFINITY : ex * m_run;
     wp.at(wave, hd, 1) = l_tot;
