@@ -21,20 +21,26 @@ constexpr int kWaves = 4;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-// Reads every 16-byte word of buf[0, n16) once (grid-stride), folds the words with
-// xor and publishes one word per workgroup into *sink so the loads stay live.
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ buf, size_t n16,
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Reads every 16-byte word of buf[0, n16) once (grid-stride, four words in flight
+// per thread, nontemporal loads: the data is not reused), folds the words with xor
+// and publishes one word per workgroup into *sink so the loads stay live.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf, size_t n16,
                                                           uint32_t* __restrict__ sink) {
   uint32_t acc = 0;
   const size_t stride = size_t(gridDim.x) * blockDim.x;
   size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    const u32x4 a = __builtin_nontemporal_load(buf + i), b = __builtin_nontemporal_load(buf + i + stride),
+                c = __builtin_nontemporal_load(buf + i + 2 * stride),
+                d = __builtin_nontemporal_load(buf + i + 3 * stride);
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3] ^ c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^
+           d[3];
   }
   for (; i < n16; i += stride) {
-    const uint4 a = buf[i];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    const u32x4 a = __builtin_nontemporal_load(buf + i);
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
   }
   for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
   __shared__ uint32_t red[4];
@@ -183,7 +189,7 @@ hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const uint4*>(buf),
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const u32x4*>(buf),
                      bytes / 16, sink);
   return hipGetLastError();
 }

@@ -651,16 +651,27 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   const int nparts = splits_of(plan, b) + wblocks;
   const float* p = part + (size_t(b) * Hq + hq) * size_t(plan.pstride) * kPartialStride;
 
+  // Batches of kBatch partials per thread: all loads of a batch are issued before
+  // any of them is used, and the merge is branch-free (empty partials have m = -inf).
+  constexpr int kBatch = 8;
   float m = -INFINITY, l = 0.0f, o = 0.0f;
-  for (int i = slice; i < nparts; i += kCombineSlices) {
-    const float* pi = p + size_t(i) * kPartialStride;
-    const float mi = pi[0], li = pi[1], oi = pi[2 + d0 + dl];
-    if (mi == -INFINITY) continue;
-    const float mn = fmaxf(m, mi);
-    const float a = m == -INFINITY ? 0.0f : exp2f(m - mn), c = exp2f(mi - mn);
-    l = l * a + li * c;
-    o = o * a + oi * c;
-    m = mn;
+  for (int i0 = slice; i0 < nparts; i0 += kCombineSlices * kBatch) {
+    float mi[kBatch], li[kBatch], oi[kBatch];
+    for (int u = 0; u < kBatch; u++) {
+      const int i = i0 + u * kCombineSlices;
+      const float* pi = p + size_t(i < nparts ? i : 0) * kPartialStride;
+      mi[u] = i < nparts ? pi[0] : -INFINITY;
+      li[u] = pi[1];
+      oi[u] = pi[2 + d0 + dl];
+    }
+    for (int u = 0; u < kBatch; u++) {
+      const float mn = fmaxf(m, mi[u]);
+      const float a = m == -INFINITY ? 0.0f : exp2f(m - mn);
+      const float c = mi[u] == -INFINITY ? 0.0f : exp2f(mi[u] - mn);
+      l = l * a + li[u] * c;
+      o = o * a + oi[u] * c;
+      m = mn;
+    }
   }
   if (dl == 0) {
     sm[slice] = m;

@@ -412,8 +412,10 @@ kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStr
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(KVQ_ERR_HIP, "device query failed: %s", hipGetErrorString(hipGetLastError()));
   const size_t n16 = bytes / 16;
-  const size_t want = (n16 + 4 * 256 - 1) / (4 * 256);  // about 4 words per thread per pass
-  const int blocks = int(std::max<size_t>(1, std::min<size_t>(want, size_t(cus) * 8)));
+  // 64 workgroups per compute unit keep enough loads in flight (measured sweep);
+  // fewer for small buffers, at least four words per thread.
+  const size_t want = (n16 + 4 * 256 - 1) / (4 * 256);
+  const int blocks = int(std::max<size_t>(1, std::min<size_t>(want, size_t(cus) * 64)));
   const hipError_t e = kvq::launch_stream_read(buf, bytes, sink, blocks, stream);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "stream read launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -520,8 +522,8 @@ kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const 
       const int b = order[p];
       const int64_t n = (Q[b] / kvq::kGroup + gps - 1) / gps;
       max_split = std::max(max_split, n);
-      plan.seq[p] = int16_t(b);
-      plan.count[b] = int16_t(n);
+      plan.seq[p] = b;
+      plan.count[b] = int32_t(n);
       plan.prefix[p + 1] = plan.prefix[p] + int32_t(n);
     }
   } else {

@@ -59,8 +59,8 @@ struct AppendArgs {
 // `pstride` slots: n_b splits, then the FP16 window's.
 struct SplitPlan {
   int32_t prefix[kInlineSeqs + 1];
-  int16_t seq[kInlineSeqs];
-  int16_t count[kInlineSeqs];
+  int32_t seq[kInlineSeqs];
+  int32_t count[kInlineSeqs];
   int32_t use_prefix;
   int32_t uniform;
   int32_t pstride;
