@@ -73,9 +73,12 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def build_caches(torch, kvq, w, copies, max_tokens, dev, gps):
+def build_caches(torch, kvq, w, copies, max_tokens, dev, gps, ev=None, stream=None):
+    """Build `copies` caches holding the workload's prefill (appends of 16384 tokens).
+    With `ev`, each copy's appends are timed (inputs drawn beforehand) and the
+    per-copy prefill times in ms are returned as well."""
     params = wl.torch_key_params(torch, w, dev)
-    caches = []
+    caches, times = [], []
     lens = w.context_lengths()
     chunk = 16384
     for c in range(copies):
@@ -86,13 +89,28 @@ def build_caches(torch, kvq, w, copies, max_tokens, dev, gps):
         gen = torch.Generator(device=dev)
         gen.manual_seed(w.seed * 1000 + c)
         done = np.zeros(w.batch, dtype=np.int64)
+        chunks = []
         while np.any(done < lens):
             n = np.minimum(lens - done, chunk)
             k, v = wl.torch_kv(torch, w, params, int(n.max()), gen, dev)
-            cache.append(k, v, n.tolist())
+            chunks.append((k, v, n.tolist()))
             done += n
+        if ev is not None:
+            a, b = ev.create(1)[0], ev.create(1)[0]
+            torch.cuda.synchronize()
+            ev.record(a, stream)
+        for k, v, n in chunks:
+            cache.append(k, v, n)
+        if ev is not None:
+            ev.record(b, stream)
+            torch.cuda.synchronize()
+            times.append(ev.elapsed_ms(a, b))
+            ev.destroy([a, b])
+        del chunks
         caches.append(cache)
     torch.cuda.synchronize()
+    if ev is not None:
+        return caches, params, times
     return caches, params
 
 
@@ -281,7 +299,23 @@ def main():
     total_steps = args.warmup + args.steps
     max_tokens = int(w.context_lengths().max()) + total_steps + 64 + 1
     print(f"[bench] building {args.copies} caches of {w.name}", file=sys.stderr, flush=True)
-    caches, params = build_caches(torch, kvq, w, args.copies, max_tokens, dev, args.groups_per_split)
+    ev = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    caches, params, prefill_ms = build_caches(torch, kvq, w, args.copies, max_tokens, dev, args.groups_per_split,
+                                              ev, stream)
+    # Prefill-side quantization throughput: every copy's prefill appends, timed.
+    lens = w.context_lengths()
+    pf_tokens = int(lens.sum())
+    pf_in_bytes = pf_tokens * w.num_kv_heads * 2 * 2 * w.head_dim
+    pf_out_per_head = sum(wl.algorithmic_bytes(int(t), int(q), w.bits, w.group, w.head_dim)
+                    for t, q in ((t, caches[0].seq_len(b)[1]) for b, t in enumerate(lens)))
+    pf_med = float(np.median(prefill_ms[1:] if len(prefill_ms) > 1 else prefill_ms))
+    prefill = {"tokens_per_sequence_max": int(lens.max()), "kv_heads": w.num_kv_heads,
+               "us": round(pf_med * 1e3, 1),
+               "tokens_per_s": round(pf_tokens / (pf_med * 1e-3), 1),
+               "input_fp16_gbps": round(pf_in_bytes / (pf_med * 1e-3) / 1e9, 1),
+               "in_plus_out_gbps": round((pf_in_bytes + pf_out_per_head * w.num_kv_heads) / (pf_med * 1e-3) / 1e9, 1),
+               "appends_of": 16384, "copies_timed": len(prefill_ms)}
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 7919)
@@ -293,8 +327,6 @@ def main():
     outs = [torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev) for _ in caches]
     torch.cuda.synchronize()
 
-    ev = HipEvents()
-    stream = torch.cuda.current_stream(dev).cuda_stream
     # Timed region: warmup steps, then exactly `steps` steps with only the two
     # bracketing events (per-step event records cost several microseconds each here).
     print(f"[bench] {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
@@ -423,6 +455,7 @@ def main():
                      "frac_of_measured_stream_read": (round(achieved / comp["hbm_stream_read_gbps"], 4)
                                                       if comp else None)},
         "comparison": comp,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -15,17 +15,21 @@ import numpy as np
 from scipy.special import softmax
 
 
-def simulate_quantized_count(T: int, R: int, G: int) -> int:
+def simulate_quantized_count(T: int, R: int, G: int, sink: bool = False) -> int:
     """Quantized-token count after appending T tokens one at a time.
 
     Rule: the most recent R tokens must stay FP16 ("Pin the most recent tokens in
     FP16"), and tokens leave the window in whole groups of G aligned to token 0.
     After each append, while the oldest FP16 group lies entirely before the last
     R tokens, it is quantized.
+
+    With an attention sink, token 0 never enters a group: the groups tile the
+    tokens after it, so only the t - 1 tokens after the sink count as history.
     """
     q = 0
     for t in range(1, T + 1):
-        while q + G <= t - R:
+        history = t - 1 if sink else t
+        while q + G <= history - R:
             q += G
     return q
 
@@ -39,14 +43,16 @@ def dense_decode(q_rows, k16, v16, head, scale=None):
     """
     T, D = k16.shape
     G = head.G
-    Qn = simulate_quantized_count(T, head.R, G)
+    sink = bool(getattr(head, "sink", False))
+    Qn = simulate_quantized_count(T, head.R, G, sink)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     keys = np.zeros((T, D))
     vals = np.zeros((T, D))
     for t in range(T):
-        if t < Qn:
-            g, i = divmod(t, G)
+        pos = t - 1 if sink else t     # position among the tokens that can be grouped
+        if 0 <= pos < Qn:
+            g, i = divmod(pos, G)
             for d in range(D):
                 keys[t, d] = float(head.kz[g][d]) + float(head.ks[g][d]) * int(head.kc[g][i, d])
                 j = d // G

@@ -291,9 +291,12 @@ def dequantize_block(kc, ks, kz, vc, vs, vz):
 # ---------------------------------------------------------------------------
 # Streaming rule and attention
 # ---------------------------------------------------------------------------
-def quantized_count(T: int, R: int, G: int = GROUP) -> int:
-    """Number of leading tokens held quantized: G * floor(max(0, T - R) / G)."""
-    return G * (max(0, T - R) // G)
+def quantized_count(T: int, R: int, G: int = GROUP, sink: bool = False) -> int:
+    """Number of tokens held quantized: G * floor(max(0, T - o - R) / G), o = 1 with
+    an attention sink (token 0 stays FP16 and groups start at token 1), else 0.
+    The quantized tokens are [o, o + count)."""
+    o = 1 if sink else 0
+    return G * (max(0, T - o - R) // G)
 
 
 def attention_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
@@ -309,10 +312,15 @@ def attention_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) ->
 
 
 class OracleHead:
-    """One (sequence, kv-head) stream: FP16 residual + quantized token groups."""
+    """One (sequence, kv-head) stream: FP16 residual + quantized token groups.
+
+    With `sink`, token 0 is an attention sink: it stays FP16 for good and the
+    groups cover tokens [1 + g G, 1 + (g + 1) G) ("KV cache quantization: putting
+    the bits in the cached vectors", full-text-skim notes: keeping the first token
+    in fp16 helps, most at 2 bits)."""
 
     def __init__(self, bits: int, residual: int, rotate: bool = False,
-                 head_dim: int = HEAD_DIM, group: int = GROUP):
+                 head_dim: int = HEAD_DIM, group: int = GROUP, sink: bool = False):
         if head_dim != HEAD_DIM or group != GROUP:
             raise ValueError("oracle block format is defined for head_dim 128, G 32")
         if residual < 0 or residual % group:
@@ -321,6 +329,8 @@ class OracleHead:
         self.R = residual
         self.G = group
         self.rotate = bool(rotate)
+        self.sink = bool(sink)
+        self.o = 1 if sink else 0   # first token of group 0
         self.k16 = np.zeros((0, head_dim), dtype=_F16)   # every appended key (rotated if asked)
         self.v16 = np.zeros((0, head_dim), dtype=_F16)
         nv = head_dim // group
@@ -350,10 +360,10 @@ class OracleHead:
             k = wht128_fp32(k.astype(_F32)).astype(_F16)
         self.k16 = np.concatenate([self.k16, k], axis=0)
         self.v16 = np.concatenate([self.v16, v], axis=0)
-        target = quantized_count(self.T, self.R, self.G)
+        target = quantized_count(self.T, self.R, self.G, self.sink)
         if self.Q >= target:
             return
-        t0, t1 = self.Q, target
+        t0, t1 = self.o + self.Q, self.o + target
         n = (t1 - t0) // self.G
         kg = self.k16[t0:t1].reshape(n, self.G, HEAD_DIM)
         vg = self.v16[t0:t1].reshape(n, self.G, HEAD_DIM // self.G, self.G)
@@ -379,16 +389,21 @@ class OracleHead:
         return t % ring_len
 
     def cache_values(self):
-        """Keys and values as attention sees them: dequantized (float64) for
-        tokens [0, Q), the stored fp16 values for tokens [Q, T)."""
+        """Keys and values as attention sees them: dequantized (float64) for the
+        quantized tokens [o, o + Q), the stored fp16 values for the rest (the window
+        [o + Q, T) and, with a sink, token 0). Attention does not depend on the
+        order of the tokens, so the sink comes last here."""
         ng = self.kc.shape[0]
         k_hat = (self.kz.astype(np.float64)[:, None, :]
                  + self.ks.astype(np.float64)[:, None, :] * self.kc.astype(np.float64))
         vs_full = np.repeat(self.vs.astype(np.float64), self.G, axis=2)
         vz_full = np.repeat(self.vz.astype(np.float64), self.G, axis=2)
         v_hat = vz_full + vs_full * self.vc.astype(np.float64)
-        k_tail = self.k16[self.Q:].astype(np.float64)
-        v_tail = self.v16[self.Q:].astype(np.float64)
+        k_tail = self.k16[self.o + self.Q:].astype(np.float64)
+        v_tail = self.v16[self.o + self.Q:].astype(np.float64)
+        if self.sink and self.T > 0:
+            k_tail = np.concatenate([k_tail, self.k16[:1].astype(np.float64)], axis=0)
+            v_tail = np.concatenate([v_tail, self.v16[:1].astype(np.float64)], axis=0)
         k_all = np.concatenate([k_hat.reshape(ng * self.G, HEAD_DIM), k_tail], axis=0)
         v_all = np.concatenate([v_hat.reshape(ng * self.G, HEAD_DIM), v_tail], axis=0)
         return k_all, v_all
@@ -414,14 +429,14 @@ class OracleCache:
     """Batch of sequences x kv-heads, mirroring the library's cache object."""
 
     def __init__(self, batch, num_q_heads, num_kv_heads, bits, residual,
-                 rotate=False, softmax_scale=None, head_dim=HEAD_DIM, group=GROUP):
+                 rotate=False, softmax_scale=None, head_dim=HEAD_DIM, group=GROUP, sink=False):
         if num_q_heads % num_kv_heads:
             raise ValueError("num_q_heads must be a multiple of num_kv_heads")
         self.B = batch
         self.Hq = num_q_heads
         self.Hkv = num_kv_heads
         self.scale = softmax_scale if softmax_scale else 1.0 / math.sqrt(head_dim)
-        self.heads = [[OracleHead(bits, residual, rotate, head_dim, group)
+        self.heads = [[OracleHead(bits, residual, rotate, head_dim, group, sink)
                        for _ in range(num_kv_heads)] for _ in range(batch)]
 
     def append(self, k, v, n_tokens=None):

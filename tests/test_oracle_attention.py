@@ -127,3 +127,92 @@ def test_ragged_append_counts():
 def test_empty_sequence_rejected():
     with pytest.raises(ValueError):
         OracleHead(2, 32).attend(np.zeros((1, 128), np.float16))
+
+
+# ---- attention sink: token 0 stays FP16, groups start at token 1 ("KV cache
+# quantization: putting the bits in the cached vectors", full-text-skim notes on
+# keeping the first token in fp16) ----
+
+@pytest.mark.parametrize("R", [0, 32, 128])
+def test_sink_count_closed_form_vs_simulation(R):
+    for T in list(range(0, 300)) + [1000, 4097]:
+        assert quantized_count(T, R, 32, sink=True) == simulate_quantized_count(T, R, 32, sink=True)
+
+
+def test_sink_window_bounds_and_first_flush():
+    for R in (0, 32, 128):
+        for T in range(R + 1, 1500):
+            fp16 = T - quantized_count(T, R, 32, sink=True)      # window plus the sink
+            assert R + 1 <= fp16 <= R + 32
+        # the first group (tokens 1..32) leaves the window when T = 1 + R + 32
+        assert quantized_count(R + 32, R, 32, sink=True) == 0
+        assert quantized_count(R + 33, R, 32, sink=True) == 32
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("R", [0, 32])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_sink_oracle_matches_bruteforce(bits, R, rotate):
+    rng = np.random.default_rng(300 + bits + R + rotate)
+    T = 140
+    k = rng.standard_normal((T, 128)).astype(np.float16)
+    k[0] *= np.float16(40.0)                       # a strong first token
+    v = rng.standard_normal((T, 128)).astype(np.float16)
+    q = rng.standard_normal((2, 128)).astype(np.float16)
+    head = OracleHead(bits, R, rotate, sink=True)
+    for a, b in [(0, 1), (1, 2), (2, 70), (70, 140)]:
+        head.append(k[a:b], v[a:b])
+    assert head.Q == simulate_quantized_count(T, R, 32, sink=True)
+    got = head.attend(q)
+    ref = dense_decode(head.prepare_query(q), head.k16, head.v16, head)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_sink_group_zero_is_tokens_1_to_32():
+    rng = np.random.default_rng(8)
+    k = rng.standard_normal((100, 128)).astype(np.float16)
+    v = rng.standard_normal((100, 128)).astype(np.float16)
+    a = OracleHead(2, 32, sink=True)
+    a.append(k, v)
+    b = OracleHead(2, 32)            # no sink, fed tokens 1..99 only
+    b.append(k[1:], v[1:])
+    assert a.Q == b.Q == 64
+    for g in range(2):
+        assert np.array_equal(a.block(g), b.block(g))
+
+
+def test_sink_small_context_is_plain_fp16_attention():
+    rng = np.random.default_rng(9)
+    T = 33                             # R + 1 tokens: nothing quantized yet
+    k = rng.standard_normal((T, 128)).astype(np.float16)
+    v = rng.standard_normal((T, 128)).astype(np.float16)
+    q = rng.standard_normal((3, 128)).astype(np.float16)
+    head = OracleHead(2, 32, sink=True)
+    head.append(k, v)
+    assert head.Q == 0
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64))[None],
+        torch.from_numpy(k.astype(np.float64))[None],
+        torch.from_numpy(v.astype(np.float64))[None])[0].numpy()
+    assert np.allclose(head.attend(q), ref, rtol=0, atol=1e-12)
+
+
+def test_sink_keeps_an_outlier_first_token_out_of_group_zero():
+    # token 0 far outside the range of the others: without a sink it shares group 0
+    # with tokens 1..31, whose per-channel range (and so their error) it blows up;
+    # with a sink it stays exact and group 0 holds ordinary tokens.
+    rng = np.random.default_rng(10)
+    T = 200
+    k = rng.standard_normal((T, 128)).astype(np.float16)
+    k[0] = np.float16(300.0)
+    v = rng.standard_normal((T, 128)).astype(np.float16)
+    with_sink = OracleHead(2, 32, sink=True)
+    without = OracleHead(2, 32)
+    for h in (with_sink, without):
+        h.append(k, v)
+    ks, _ = with_sink.cache_values()
+    kn, _ = without.cache_values()
+    exact = k.astype(np.float64)
+    assert np.array_equal(ks[-1], exact[0])                   # the sink comes last
+    assert np.abs(kn[1:32] - exact[1:32]).max() > 3.0          # group 0 without a sink
+    assert np.abs(ks[0:31] - exact[1:32]).max() < 1.5          # group 0 with a sink = tokens 1..32
