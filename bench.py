@@ -157,14 +157,14 @@ def measure_comparisons(torch, kvq, w, ev, stream, dev, iters=20):
     res = {}
     buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
     buf.fill_(1)
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    fold = torch.zeros(1, dtype=torch.int32, device=dev)
     for _ in range(2):
-        kvq.stream_read(buf, sink)
+        kvq.stream_read(buf, fold)
     torch.cuda.synchronize()
     a, b = ev.create(1)[0], ev.create(1)[0]
     ev.record(a, stream)
     for _ in range(iters):
-        kvq.stream_read(buf, sink)
+        kvq.stream_read(buf, fold)
     ev.record(b, stream)
     torch.cuda.synchronize()
     res["hbm_stream_read_gbps"] = round(buf.numel() * iters / (ev.elapsed_ms(a, b) * 1e-3) / 1e9, 1)

@@ -46,6 +46,7 @@ class KVQConfig(ctypes.Structure):
         ("rotate", ctypes.c_int32),
         ("max_tokens", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float),
+        ("sink", ctypes.c_int32),
     ]
 
 
@@ -112,10 +113,11 @@ def check(status: int) -> None:
 
 
 def make_config(batch, num_q_heads, num_kv_heads, head_dim=128, bits=2, group=32, residual=128,
-                rotate=False, max_tokens=4096, softmax_scale=0.0) -> KVQConfig:
-    return KVQConfig(batch, num_q_heads, num_kv_heads, head_dim, bits, group, residual,
-                     int(bool(rotate)) if rotate in (True, False) else int(rotate),
-                     max_tokens, softmax_scale)
+                rotate=False, max_tokens=4096, softmax_scale=0.0, sink=False) -> KVQConfig:
+    def flag(x):
+        return int(bool(x)) if x in (True, False) else int(x)
+    return KVQConfig(batch, num_q_heads, num_kv_heads, head_dim, bits, group, residual, flag(rotate),
+                     max_tokens, softmax_scale, flag(sink))
 
 
 def cache_bytes(cfg: KVQConfig) -> int:
@@ -136,11 +138,11 @@ class KVCache:
     """A low-bit KV cache on one GPU, owning its device memory as a torch tensor."""
 
     def __init__(self, batch, num_q_heads, num_kv_heads, head_dim=128, bits=2, group=32, residual=128,
-                 rotate=False, max_tokens=4096, softmax_scale=0.0, device="cuda"):
+                 rotate=False, max_tokens=4096, softmax_scale=0.0, device="cuda", sink=False):
         import torch
         self._torch = torch
         self.cfg = make_config(batch, num_q_heads, num_kv_heads, head_dim, bits, group, residual,
-                               rotate, max_tokens, softmax_scale)
+                               rotate, max_tokens, softmax_scale, sink)
         self.device = torch.device(device)
         nbytes = cache_bytes(self.cfg)
         self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -157,7 +159,7 @@ class KVCache:
 
     @property
     def ring_len(self):
-        return self.cfg.residual + self.cfg.group
+        return self.cfg.residual + self.cfg.group + self.cfg.sink
 
     def _check_tensor(self, t, shape, dtype, name):
         torch = self._torch
@@ -271,12 +273,12 @@ class KVCache:
 
 # -- comparison kernels -------------------------------------------------------
 
-def stream_read(buf, sink):
+def stream_read(buf, fold):
     """Stream-read every byte of the device tensor `buf` once; xor a fold into the
-    int32 device tensor `sink` (one element). Asynchronous on the current stream."""
+    int32 device tensor `fold` (one element). Asynchronous on the current stream."""
     import torch
     check(load().kvq_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
-                                 ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(_stream_ptr(torch, buf.device))))
+                                 ctypes.c_void_p(fold.data_ptr()), ctypes.c_void_p(_stream_ptr(torch, buf.device))))
 
 
 class Fp16Decode:

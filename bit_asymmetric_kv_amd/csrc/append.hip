@@ -103,7 +103,8 @@ template <int BITS>
 __global__ __launch_bounds__(256) void flush_kernel(uint8_t* __restrict__ blocks, const __half* __restrict__ ringk,
                                                     const __half* __restrict__ ringv, const SeqArgs seq,
                                                     const __half* __restrict__ kin, const __half* __restrict__ vin,
-                                                    int Hkv, int W, long long gcap, int n_max, int rotate) {
+                                                    int Hkv, int W, int RS, int sink, long long gcap, int n_max,
+                                                    int rotate) {
   constexpr int CB = kG * kD * BITS / 8;  // bytes of one code section
   constexpr int GB = 2 * CB + 1024;
   __shared__ float xk[kG][kD + 1];
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void flush_kernel(uint8_t* __restrict__ blocks
   const int nflush = (sd.q_new - sd.q_old) / kG;
   if (int(blockIdx.x) >= nflush) return;
   const int g = sd.q_old / kG + blockIdx.x;
-  const int t0 = g * kG;
+  const int t0 = sink + g * kG;  // with an attention sink, group g starts at token 1 + 32 g
   const size_t bh = size_t(b) * Hkv + h;
 
   if (threadIdx.x < kG) from_input[threadIdx.x] = (t0 + int(threadIdx.x) >= sd.t_old) ? 1 : 0;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void flush_kernel(uint8_t* __restrict__ blocks
     int t = t0 + i;
     __half kv, vv;
     if (t < sd.t_old) {
-      size_t off = (bh * W + size_t(t % W)) * kD + d;
+      size_t off = (bh * RS + size_t(t % W)) * kD + d;
       kv = ringk[off];
       vv = ringv[off];
     } else {
@@ -198,23 +199,27 @@ __global__ __launch_bounds__(256) void flush_kernel(uint8_t* __restrict__ blocks
   }
 }
 
-// One block per (appended token that stays in the FP16 window, kv-head, sequence).
+// One block per (appended token that stays in FP16, kv-head, sequence). Window
+// token t (t >= o) goes to ring slot t % W; an attention sink (token 0, appended by
+// the first append of the sequence) goes to slot W and takes block 0.
 __global__ __launch_bounds__(128) void ring_write_kernel(__half* __restrict__ ringk, __half* __restrict__ ringv,
                                                          const SeqArgs seq, const __half* __restrict__ kin,
-                                                         const __half* __restrict__ vin, int Hkv, int W, int n_max,
-                                                         int rotate) {
+                                                         const __half* __restrict__ vin, int Hkv, int W, int RS,
+                                                         int sink, int n_max, int rotate) {
   __shared__ float row[kD];
   __shared__ int one;
   const int h = blockIdx.y, b = blockIdx.z;
   const SeqDesc sd = seq.inl_valid ? seq.inl[b] : seq.dev[b];
   if (seq.inl_valid && blockIdx.x == 0 && h == 0 && threadIdx.x == 0) seq.state[b] = sd;
   const int t_new = sd.t_old + sd.n_new;
-  const int first = max(sd.t_old, sd.q_new);
-  const int t = first + blockIdx.x;
+  const int sink_new = (sink && sd.t_old == 0 && sd.n_new > 0) ? 1 : 0;
+  const int first = max(sd.t_old, sink + sd.q_new);
+  const bool is_sink = sink_new && blockIdx.x == 0;
+  const int t = is_sink ? 0 : first + int(blockIdx.x) - sink_new;
   if (t >= t_new) return;
   const int d = threadIdx.x;
   size_t in_off = ((size_t(b) * n_max + (t - sd.t_old)) * Hkv + h) * kD + d;
-  size_t out_off = ((size_t(b) * Hkv + h) * W + size_t(t % W)) * kD + d;
+  size_t out_off = ((size_t(b) * Hkv + h) * RS + size_t(is_sink ? W : t % W)) * kD + d;
   ringv[out_off] = vin[in_off];
   if (!rotate) {
     ringk[out_off] = kin[in_off];
@@ -239,10 +244,10 @@ hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqArgs& seq, cons
   auto* vin = static_cast<const __half*>(v);
   if (L.bits == 2)
     hipLaunchKernelGGL(flush_kernel<2>, grid, dim3(256), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
-                       (long long)L.gcap, n_max, rotate);
+                       L.RS, L.sink, (long long)L.gcap, n_max, rotate);
   else
     hipLaunchKernelGGL(flush_kernel<4>, grid, dim3(256), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
-                       (long long)L.gcap, n_max, rotate);
+                       L.RS, L.sink, (long long)L.gcap, n_max, rotate);
   return hipGetLastError();
 }
 
@@ -251,7 +256,7 @@ hipError_t launch_ring_write(const Layout& L, uint8_t* base, const SeqArgs& seq,
   dim3 grid(max_ring_tokens, L.Hkv, L.B);
   hipLaunchKernelGGL(ring_write_kernel, grid, dim3(kD), 0, stream, reinterpret_cast<__half*>(base + L.ringk_off),
                      reinterpret_cast<__half*>(base + L.ringv_off), seq, static_cast<const __half*>(k),
-                     static_cast<const __half*>(v), L.Hkv, L.W, n_max, rotate);
+                     static_cast<const __half*>(v), L.Hkv, L.W, L.RS, L.sink, n_max, rotate);
   return hipGetLastError();
 }
 

@@ -25,9 +25,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Reads every 16-byte word of buf[0, n16) once (grid-stride, four words in flight
 // per thread, nontemporal loads: the data is not reused), folds the words with xor
-// and publishes one word per workgroup into *sink so the loads stay live.
+// and publishes one word per workgroup into *fold so the loads stay live.
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf, size_t n16,
-                                                          uint32_t* __restrict__ sink) {
+                                                          uint32_t* __restrict__ fold) {
   uint32_t acc = 0;
   const size_t stride = size_t(gridDim.x) * blockDim.x;
   size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   __shared__ uint32_t red[4];
   if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) atomicXor(sink, red[0] ^ red[1] ^ red[2] ^ red[3]);
+  if (threadIdx.x == 0) atomicXor(fold, red[0] ^ red[1] ^ red[2] ^ red[3]);
 }
 
 struct Fp16Args {
@@ -188,9 +188,9 @@ hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream) {
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* fold, int blocks, hipStream_t stream) {
   hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const u32x4*>(buf),
-                     bytes / 16, sink);
+                     bytes / 16, fold);
   return hipGetLastError();
 }
 

@@ -48,7 +48,8 @@ struct DecodeArgs {
   float* part;
   long long gcap;
   int B, Hkv, Hq, W, gps, rotate;
-  int wblocks;  // FP16-window workgroups per (sequence, kv-head)
+  int RS, sink;  // ring slots per (sequence, kv-head): W, plus slot W for an attention sink
+  int wblocks;   // FP16-window workgroups per (sequence, kv-head)
   SplitPlan plan;  // split workgroups per sequence and the partial slots per query head
   AppendArgs app;  // an append folded into this launch (app.pending)
   float scale_log2;
@@ -241,16 +242,18 @@ __device__ void merge_and_store(const DecodeArgs& a, int b, int h, int split, co
   }
 }
 
-// Attention of the HG query heads over one chunk of at most 32 tokens of the FP16
-// window, tokens [t0, t0 + cnt), computed by one wave; the wave's partial (m, l, o)
-// goes to its slot of `wp`. All loads of the chunk are issued first. Scores: lane l
-// takes token l % 32 and channel half l / 32. Weighted values: lane l accumulates
+// Attention of the HG query heads over one chunk of at most 32 FP16 tokens,
+// tokens [t0, t0 + cnt), computed by one wave; the wave's partial (m, l, o) goes to
+// its slot of `wp`. Token t0 + i sits in ring slot s0 + i, less W once that reaches
+// `wlim` (W for the window, whose token t is in slot t % W; W + 1 for the attention
+// sink, in slot W). All loads of the chunk are issued first. Scores: lane l takes
+// token l % 32 and channel half l / 32. Weighted values: lane l accumulates
 // channels 2l and 2l + 1 over the chunk's tokens.
 // With an append folded into the launch (caches without rotation), tokens
 // t >= t_old come from the appended rows and are written to the ring.
 template <int HG>
-__device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt, int t_old, const float (*qf)[kD],
-                             const float* expo, const WaveParts& wp, int wave, int lane) {
+__device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt, int s0, int wlim, int t_old,
+                             const float (*qf)[kD], const float* expo, const WaveParts& wp, int wave, int lane) {
   if (cnt <= 0) {
     if (lane < HG) {
       wp.at(wave, lane, 0) = -INFINITY;
@@ -258,8 +261,7 @@ __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt,
     }
     return;
   }
-  const size_t row0 = (size_t(b) * a.Hkv + h) * size_t(a.W);
-  const int s0 = t0 % a.W;
+  const size_t row0 = (size_t(b) * a.Hkv + h) * size_t(a.RS);
   const int tl = lane % 32, hf = lane / 32;
   const bool kval = tl < cnt;
   const bool pend = a.app.pending != 0;
@@ -270,7 +272,7 @@ __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt,
   const int tk = t0 + (kval ? tl : 0);
   const bool knew = pend && tk >= t_old;
   int kslot = s0 + (kval ? tl : 0);
-  if (kslot >= a.W) kslot -= a.W;
+  if (kslot >= wlim) kslot -= a.W;
   uint4 kr[8];
   {
     const __half* src = knew ? kin + in_row(tk) : a.ringk + (row0 + kslot) * kD;
@@ -281,7 +283,7 @@ __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt,
   for (int t = 0; t < kG; t++) {
     const int tt = t0 + (t < cnt ? t : 0);
     int slot = s0 + (t < cnt ? t : 0);
-    if (slot >= a.W) slot -= a.W;
+    if (slot >= wlim) slot -= a.W;
     const __half* src = pend && tt >= t_old ? vin + in_row(tt) : a.ringv + (row0 + slot) * kD;
     vr[t] = *reinterpret_cast<const uint32_t*>(src + 2 * lane);
   }
@@ -299,7 +301,7 @@ __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt,
     }
     for (int t = max(0, t_old - t0); t < cnt; t++) {
       int slot = s0 + t;
-      if (slot >= a.W) slot -= a.W;
+      if (slot >= wlim) slot -= a.W;
       *reinterpret_cast<uint32_t*>(a.ringv + (row0 + slot) * kD + 2 * lane) = vr[t];
     }
   }
@@ -448,10 +450,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   if (tail || a.rotate) prepare_query<HG>(a, b, h, qf, expo);
 
   if (tail) {
-    // Window workgroup wsub takes chunks 4 * wsub + wave of the window [Q, T).
+    // Window workgroup wsub takes chunk 4 * wsub + wave: with an attention sink,
+    // chunk 0 is the sink (token 0, ring slot W) and chunk c >= 1 holds tokens
+    // [o + Q + 32 (c - 1), ...) of the window; without one, chunk c holds
+    // [Q + 32 c, ...). Window token t is in ring slot t % W.
     const int chunk = (split - nsb) * kWaves + wave;
-    const int t0 = Q + chunk * kG;
-    window_chunk<HG>(a, b, h, t0, min(kG, T - t0), sd.t_old, qf, expo, wp, wave, lane);
+    if (a.sink && chunk == 0) {
+      window_chunk<HG>(a, b, h, 0, min(1, T), a.W, a.W + 1, sd.t_old, qf, expo, wp, wave, lane);
+    } else {
+      const int t0 = a.sink + Q + (chunk - a.sink) * kG;
+      window_chunk<HG>(a, b, h, t0, min(kG, T - t0), t0 % a.W, a.W, sd.t_old, qf, expo, wp, wave, lane);
+    }
     // A folded append with inline records: store them as the sequence's state.
     if (a.app.pending && a.app.seq.inl_valid && h == 0 && split == nsb && threadIdx.x == 0)
       a.app.seq.state[b] = sd;
@@ -737,6 +746,8 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   a.Hkv = L.Hkv;
   a.Hq = L.Hq;
   a.W = L.W;
+  a.RS = L.RS;
+  a.sink = L.sink;
   a.gps = groups_per_split;
   a.plan = plan;
   a.app = app;

@@ -35,9 +35,10 @@ kvq_status ok() {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Quantized-token count of the residual rule: G * floor(max(0, T - R) / G).
-int64_t quantized_count(int64_t T, int64_t R) {
-  int64_t over = T - R;
+// Quantized-token count of the residual rule: G * floor(max(0, T - o - R) / G), o = 1
+// with an attention sink (its groups start at token 1).
+int64_t quantized_count(int64_t T, int64_t R, int sink) {
+  int64_t over = T - sink - R;
   if (over <= 0) return 0;
   return (over / kvq::kGroup) * kvq::kGroup;
 }
@@ -66,6 +67,7 @@ kvq_status validate(const kvq_config* cfg) {
   if (cfg->rotate != 0 && cfg->rotate != 1) return fail(KVQ_ERR_INVALID_ARG, "rotate must be 0 or 1");
   if (cfg->max_tokens < 1 || cfg->max_tokens > (int64_t(1) << 30))
     return fail(KVQ_ERR_INVALID_ARG, "max_tokens must be in [1, 2^30]");
+  if (cfg->sink != 0 && cfg->sink != 1) return fail(KVQ_ERR_INVALID_ARG, "sink must be 0 or 1");
   if (!(cfg->softmax_scale >= 0.0f) || std::isinf(cfg->softmax_scale))
     return fail(KVQ_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   return ok();
@@ -79,18 +81,20 @@ Layout make_layout(const kvq_config* cfg) {
   L.bits = cfg->bits;
   L.R = cfg->residual;
   L.W = cfg->residual + kvq::kGroup;
+  L.sink = cfg->sink;
+  L.RS = L.W + L.sink;
   L.gcap = (cfg->max_tokens + kvq::kGroup - 1) / kvq::kGroup;
   L.group_bytes = kvq_group_bytes(cfg->bits);
   int64_t ms = (L.gcap + kvq::kMinGroupsPerSplit - 1) / kvq::kMinGroupsPerSplit;
   L.max_splits = int32_t(std::max<int64_t>(1, std::min<int64_t>(ms, kvq::kMaxSplits)));
-  const int32_t win_chunks = L.R / kvq::kGroup + 1;  // the window holds < R + G tokens
+  const int32_t win_chunks = L.R / kvq::kGroup + 1 + L.sink;  // window < R + G tokens, plus the sink
   L.win_blocks = (win_chunks + kvq::kWindowChunksPerBlock - 1) / kvq::kWindowChunksPerBlock;
   size_t off = 0;
   L.seq_off = off;
   off = align256(off + sizeof(SeqDesc) * size_t(L.B));
   L.blocks_off = off;
   off = align256(off + size_t(L.B) * L.Hkv * size_t(L.gcap) * L.group_bytes);
-  size_t ring = size_t(L.B) * L.Hkv * L.W * kvq::kHeadDim * 2;
+  size_t ring = size_t(L.B) * L.Hkv * L.RS * kvq::kHeadDim * 2;
   L.ringk_off = off;
   off = align256(off + ring);
   L.ringv_off = off;
@@ -281,15 +285,17 @@ kvq_status prepare_append(kvq_cache* c, const void* k, const void* v, const int3
   for (int b = 0; b < B; b++) {
     int64_t n = n_tokens ? n_tokens[b] : n_max;
     pa.T2[b] = c->T[b] + n;
-    pa.Q2[b] = quantized_count(pa.T2[b], c->cfg.residual);
+    pa.Q2[b] = quantized_count(pa.T2[b], c->cfg.residual, c->cfg.sink);
     d[b].t_old = int32_t(c->T[b]);
     d[b].n_new = int32_t(n);
     d[b].q_old = int32_t(c->Q[b]);
     d[b].q_new = int32_t(pa.Q2[b]);
     pa.max_flush = std::max<int32_t>(pa.max_flush, int32_t((pa.Q2[b] - c->Q[b]) / kvq::kGroup));
-    // appended tokens that stay in the FP16 window
-    int64_t first_kept = std::max<int64_t>(c->T[b], pa.Q2[b]);
-    pa.max_ring = std::max<int32_t>(pa.max_ring, int32_t(std::max<int64_t>(0, pa.T2[b] - first_kept)));
+    // appended tokens that stay in the FP16 window (an appended sink counts as one more)
+    int64_t first_kept = std::max<int64_t>(c->T[b], c->cfg.sink + pa.Q2[b]);
+    const int64_t sink_new = (c->cfg.sink && c->T[b] == 0 && n > 0) ? 1 : 0;
+    pa.max_ring = std::max<int32_t>(pa.max_ring,
+                                    int32_t(std::max<int64_t>(0, pa.T2[b] - first_kept) + sink_new));
   }
   SeqDesc* dev_seq = reinterpret_cast<SeqDesc*>(c->base + c->L.seq_off);
   pa.sa.dev = dev_seq;
@@ -383,7 +389,7 @@ kvq_status kvq_read_state(kvq_cache* c, int32_t part, int32_t b, int32_t h, size
       break;
     case KVQ_PART_RING_K:
     case KVQ_PART_RING_V:
-      region = size_t(L.W) * kvq::kHeadDim * 2;
+      region = size_t(L.RS) * kvq::kHeadDim * 2;
       start = (part == KVQ_PART_RING_K ? L.ringk_off : L.ringv_off) + bh * region;
       break;
     default:
@@ -399,8 +405,8 @@ kvq_status kvq_read_state(kvq_cache* c, int32_t part, int32_t b, int32_t h, size
   return ok();
 }
 
-kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
-  if (!buf || !sink) return fail(KVQ_ERR_INVALID_ARG, "buf and sink must be device pointers");
+kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* fold, hipStream_t stream) {
+  if (!buf || !fold) return fail(KVQ_ERR_INVALID_ARG, "buf and fold must be device pointers");
   if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
     return fail(KVQ_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and buf 16-byte aligned");
   int ndev = 0, dev = 0, cus = 0;
@@ -416,7 +422,7 @@ kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStr
   // fewer for small buffers, at least four words per thread.
   const size_t want = (n16 + 4 * 256 - 1) / (4 * 256);
   const int blocks = int(std::max<size_t>(1, std::min<size_t>(want, size_t(cus) * 64)));
-  const hipError_t e = kvq::launch_stream_read(buf, bytes, sink, blocks, stream);
+  const hipError_t e = kvq::launch_stream_read(buf, bytes, fold, blocks, stream);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "stream read launch failed: %s", hipGetErrorString(e));
   return ok();
 }

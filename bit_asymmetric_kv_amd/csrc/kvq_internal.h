@@ -12,10 +12,11 @@ constexpr int kPartialStride = kHeadDim + 2;  // m (log2 domain), l, o[128] per 
 constexpr int kMinGroupsPerSplit = 4;
 constexpr int kMaxSplits = 2048;
 constexpr int kMaxResidual = 4096;
-// The FP16 window [Q, T) holds at most residual + group - 1 tokens: residual / 32 + 1
-// chunks of 32 tokens, four per decode workgroup.
+// The FP16 window [o + Q, T) holds at most residual + group - 1 tokens: residual / 32
+// + 1 chunks of 32 tokens, plus one chunk for an attention sink; four chunks per
+// decode workgroup.
 constexpr int kWindowChunksPerBlock = 4;
-constexpr int kMaxWindowBlocks = (kMaxResidual / kGroup + 1 + kWindowChunksPerBlock - 1) / kWindowChunksPerBlock;
+constexpr int kMaxWindowBlocks = (kMaxResidual / kGroup + 2 + kWindowChunksPerBlock - 1) / kWindowChunksPerBlock;
 
 // Per-sequence record kept on the device and rewritten by every append:
 // tokens before the append, tokens appended, quantized tokens before and after.
@@ -67,7 +68,9 @@ struct SplitPlan {
 };
 
 struct Layout {
-  int32_t B, Hq, Hkv, bits, R, W;  // W = R + G ring slots
+  int32_t B, Hq, Hkv, bits, R, W;  // W = R + G window slots (token t >= o in slot t % W)
+  int32_t sink;                     // 1: token 0 is an attention sink, kept in ring slot W
+  int32_t RS;                       // ring slots per (b, h): W + sink
   int64_t gcap;                     // group blocks per (b, h)
   size_t group_bytes;
   int32_t max_splits;
@@ -96,7 +99,7 @@ hipError_t launch_combine(const float* part, float* out, int Hq, int B, const Sp
 
 // Comparison kernels: streaming read of a buffer; decode over a plain FP16 cache
 // [B][Hkv][t_cap][128] (partials [B][Hq][nsplit][130] in `part`).
-hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* fold, int blocks, hipStream_t stream);
 hipError_t launch_fp16_decode(const void* k, const void* v, const int32_t* lens, long long t_cap, int B, int Hq,
                               int Hkv, float scale_log2, const void* q, float* out, float* part, int nsplit,
                               int cps, hipStream_t stream);

@@ -24,8 +24,9 @@
  *  - quantizer (fp32): s32 = (max - min) / (2^b - 1); s = fp16(s32) and
  *    z = fp16(min) are stored; code = clamp(rint_half_even((x - z) * (1 / s)),
  *    0, 2^b - 1) with every operation rounded to fp32; s == 0 gives all-zero codes;
- *  - residual rule: after every append, Q = G * floor(max(0, T - R) / G) tokens
- *    are quantized and tokens [Q, T) stay FP16 (R to R + G - 1 of them);
+ *  - residual rule: after every append, Q = G * floor(max(0, T - o - R) / G)
+ *    tokens [o, o + Q) are quantized and tokens [o + Q, T) stay FP16 (R to R + G - 1
+ *    of them), o = 1 with an attention sink (token 0 then stays FP16 too), else 0;
  *  - rotation: natural-order butterflies in fp32, then a multiply by
  *    fp32(1/sqrt(128)); rotated keys are rounded to fp16 before storage, the
  *    rotated query is kept in fp32, values are not rotated;
@@ -76,6 +77,10 @@ typedef struct {
   int32_t rotate;        /* 0 or 1: normalized Walsh-Hadamard transform on q and k */
   int64_t max_tokens;    /* per-sequence capacity, 1 .. 2^30 */
   float softmax_scale;   /* 0 => 1/sqrt(head_dim) */
+  int32_t sink;          /* 0 or 1: token 0 of every sequence is an attention sink kept in FP16 for
+                            good; groups then cover tokens [1 + gG, 1 + (g+1)G) ("KV cache
+                            quantization: putting the bits in the cached vectors", full-text-skim
+                            notes: keeping the first token in fp16 helps, most at 2 bits) */
 } kvq_config;
 
 /* Bytes of device memory a cache with this configuration needs (host only).
@@ -134,13 +139,15 @@ kvq_status kvq_set_profile_events(kvq_cache* c, hipEvent_t start, hipEvent_t sto
  * frees library-allocated memory. */
 void kvq_destroy(kvq_cache* c);
 
-/* Host mirror of sequence b: T = tokens appended, Q = tokens held quantized. */
+/* Host mirror of sequence b: T = tokens appended, Q = tokens held quantized
+ * (tokens [o, o + Q), o = 1 with an attention sink, else 0). */
 kvq_status kvq_seq_len(const kvq_cache* c, int32_t b, int64_t* T, int64_t* Q);
 
 /* Parts of the state that kvq_read_state can copy out. */
 enum {
   KVQ_PART_GROUPS = 0, /* packed group blocks of (b, h): group g at byte g * kvq_group_bytes() */
-  KVQ_PART_RING_K = 1, /* FP16 key window of (b, h): [R + G][D], token t in slot t % (R + G) */
+  KVQ_PART_RING_K = 1, /* FP16 key window of (b, h): [R + G + sink][D], token t in slot
+                          t % (R + G), except an attention sink (token 0) in slot R + G */
   KVQ_PART_RING_V = 2  /* FP16 value window of (b, h), same layout */
 };
 
@@ -169,12 +176,12 @@ const char* kvq_last_error(void);
 
 /* Streaming-read probe: reads each 16-byte word of the device buffer buf[0, bytes)
  * once with vector loads spread over the whole GPU and xors a fold of the words
- * into the device word *sink (the caller clears it first if it wants the fold), so
+ * into the device word *fold (the caller clears it first if it wants the fold), so
  * the loads cannot be elided. Timing it gives the achievable HBM read bandwidth to
  * set the decode kernel's effective bandwidth against (the nominal peak is a
  * datasheet figure). bytes: positive multiple of 16; buf 16-byte aligned.
  * Asynchronous on `stream`. */
-kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* fold, hipStream_t stream);
 
 /* Decode attention over a plain FP16 KV cache, the full-precision decode that the
  * pages set low-bit caches against (flash-decoding over the whole cache: "Read

@@ -45,6 +45,7 @@ class Workload:
     seed: int
     ragged: tuple = field(default=())   # (lo, hi) inclusive per-sequence context range
     head_dim: int = HEAD_DIM
+    sink: bool = False           # token 0 kept FP16 as an attention sink
 
     def context_lengths(self) -> np.ndarray:
         """Prefill length of every sequence."""

@@ -27,10 +27,11 @@ class Pair:
         self.torch = torch
         self.dev = device
         self.gpu = kvq.KVCache(w.batch, w.num_q_heads, w.num_kv_heads, bits=w.bits, group=w.group,
-                               residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=device)
+                               residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=device,
+                               sink=w.sink)
         if groups_per_split:
             self.gpu.set_decode_split(groups_per_split)
-        self.ref = OracleCache(w.batch, w.num_q_heads, w.num_kv_heads, w.bits, w.residual, w.rotate)
+        self.ref = OracleCache(w.batch, w.num_q_heads, w.num_kv_heads, w.bits, w.residual, w.rotate, sink=w.sink)
         self.T = np.zeros(w.batch, dtype=np.int64)
         self.step = 0
 
@@ -62,15 +63,18 @@ class Pair:
             W = w.residual + w.group
             rk = self.gpu.read_ring(b, h, "k")
             rv = self.gpu.read_ring(b, h, "v")
-            for t in range(Q, T):
-                gk, ok_ = rk[t % W], oh.k16[t]
+            o = 1 if w.sink else 0
+            # window tokens [o + Q, T) in slot t % W; an attention sink (token 0) in slot W
+            slots = [(t, t % W) for t in range(o + Q, T)] + ([(0, W)] if w.sink and T > 0 else [])
+            for t, slot in slots:
+                gk, ok_ = rk[slot], oh.k16[t]
                 if not np.array_equal(gk.view(np.uint16), ok_.view(np.uint16)):
                     bad = np.nonzero(gk.view(np.uint16) != ok_.view(np.uint16))[0]
                     raise AssertionError(
-                        f"ring key (b={b}, h={h}, t={t}, slot {t % W}, T={T}, Q={Q}) differs in {len(bad)} "
+                        f"ring key (b={b}, h={h}, t={t}, slot {slot}, T={T}, Q={Q}) differs in {len(bad)} "
                         f"channels {bad[:6].tolist()}: gpu {gk[bad[:4]].tolist()} oracle {ok_[bad[:4]].tolist()}")
-                assert np.array_equal(rv[t % W].view(np.uint16), oh.v16[t].view(np.uint16)), \
-                    f"ring value (b={b}, h={h}, t={t})"
+                assert np.array_equal(rv[slot].view(np.uint16), oh.v16[t].view(np.uint16)), \
+                    f"ring value (b={b}, h={h}, t={t}, slot {slot})"
 
     def decode(self):
         q = wl.queries(self.w, self.step)

@@ -41,7 +41,8 @@ def _status(cfg):
 @pytest.mark.parametrize("field,value", [
     ("batch", 0), ("num_kv_heads", 0), ("num_q_heads", 12), ("head_dim", 64), ("bits", 3), ("bits", 8),
     ("group", 64), ("residual", 48), ("residual", -32), ("rotate", 2), ("max_tokens", 0),
-    ("max_tokens", 1 << 31), ("softmax_scale", -1.0), ("softmax_scale", float("inf")),
+    ("max_tokens", 1 << 31), ("softmax_scale", -1.0), ("softmax_scale", float("inf")), ("sink", 2),
+    ("sink", -1),
 ])
 def test_invalid_configs_rejected_before_any_device_call(field, value):
     cfg = kvq.make_config(2, 32, 8, residual=128, max_tokens=1000)
@@ -86,6 +87,9 @@ def test_cache_bytes_grows_with_capacity_and_holds_the_blocks():
     assert big >= 8 * 32768 * 3072
     four = kvq.cache_bytes(kvq.make_config(1, 32, 8, bits=4, residual=128, max_tokens=131072))
     assert four - small >= 8 * 4096 * (5120 - 3072)
+    # an attention sink adds one FP16 key and value row per (sequence, kv-head)
+    sink = kvq.cache_bytes(kvq.make_config(1, 32, 8, residual=128, max_tokens=131072, sink=True))
+    assert sink - small >= 8 * 2 * 128 * 2
 
 
 def test_comparison_entry_points_validate_on_the_host():
@@ -110,7 +114,7 @@ def test_comparison_entry_points_validate_on_the_host():
     # null pointers
     assert lib.kvq_fp16_decode_attention(ctypes.byref(cfg), None, fake, fake, 100, fake, fake, fake, 1 << 30,
                                          None) == _lib.KVQ_ERR_INVALID_ARG
-    # stream read: size not a multiple of 16, misaligned buffer, null sink
+    # stream read: size not a multiple of 16, misaligned buffer, null fold word
     assert lib.kvq_stream_read(fake, 100, fake, None) == _lib.KVQ_ERR_INVALID_ARG
     assert lib.kvq_stream_read(ctypes.c_void_p(264), 1024, fake, None) == _lib.KVQ_ERR_INVALID_ARG
     assert lib.kvq_stream_read(fake, 1024, None, None) == _lib.KVQ_ERR_INVALID_ARG

@@ -25,11 +25,11 @@ def test_stream_read_fold(dev, words):
     rng = np.random.default_rng(words)
     host = rng.integers(0, 2**32, size=words, dtype=np.uint32)
     buf = torch.from_numpy(host.view(np.int32)).to(dev)
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    fold = torch.zeros(1, dtype=torch.int32, device=dev)
     print(f"case stream_read words={words}", flush=True)
-    kvq.stream_read(buf, sink)
+    kvq.stream_read(buf, fold)
     torch.cuda.synchronize()
-    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host))
+    assert int(fold.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host))
 
 
 def _fp16_case(dev, B, Hq, Hkv, lens, t_cap, seed, scale=0.0):
