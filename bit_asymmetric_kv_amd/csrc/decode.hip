@@ -445,6 +445,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       G.vz[jr] = load_half8(blk + 2 * CB + 768 + 16 * (kb_ * 4 + jbase_ + jr));
     }
   };
+  // The first three groups' loads go out before the query is read, so that the two
+  // memory round trips overlap.
+  GroupRegs<BITS, NJ> R0, R1, R2, R3;
+  if (n > 0) {
+    load_group(0, R0);
+    load_group(min(1, n - 1), R1);
+    load_group(min(2, n - 1), R2);
+  }
+
   // The FP16-window workgroup and rotated queries use the shared-memory query
   // preparation; otherwise each wave prepares what its lanes need on its own.
   if (tail || a.rotate) prepare_query<HG>(a, b, h, qf, expo);
@@ -526,8 +535,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // The group loop is software-pipelined: while group r's softmax and value side run,
   // group r+1's key-side scores are computed (its bytes are already in registers)
   // and group r+2's bytes are on their way, so the dependency chains overlap.
-  GroupRegs<BITS, NJ> G;   // group whose scores are in s0 / s1
-  float4v s0, s1;
+  float4v s0, s1;  // key-side scores of the group whose value side runs next
 
   // Key side, first half: q' = q * s_key per channel as fp16 high + low parts, to
   // shared memory in the MFMA B layout, and q . z_key per head (returned for this
@@ -609,21 +617,45 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  GroupRegs<BITS, NJ> Gn, Gnn;
+  // Four register sets R0..R3 take the roles (group r, r+1, r+2, r+3) in turn, so nothing
+  // is copied between them: the loads of group r+3, issued in stage r, are first
+  // used in stage r+2 and have two stages to land. Loads past the last group
+  // re-read the last group (same bytes; always issued, so the count of loads in
+  // flight is the same in every stage).
+  auto stage = [&](int r, const GroupRegs<BITS, NJ>& Gr, const GroupRegs<BITS, NJ>& Gr1,
+                   GroupRegs<BITS, NJ>& Gr3) {
+    load_group(min(r + 3, n - 1), Gr3);
+    const float qzn = key_prep(Gr1);
+    value_side(Gr, s0, s1);
+    key_mfma(Gr1, qzn, s0, s1);
+  };
   if (n > 0) {
-    load_group(0, G);
-    if (n > 1) load_group(1, Gn);
-    key_mfma(G, key_prep(G), s0, s1);
+    key_mfma(R0, key_prep(R0), s0, s1);
+    int r = 0;
+    for (; r + 4 < n; r += 4) {
+      stage(r, R0, R1, R3);
+      stage(r + 1, R1, R2, R0);
+      stage(r + 2, R2, R3, R1);
+      stage(r + 3, R3, R0, R2);
+    }
+    // n - 1 - r (0 to 3) stages remain; the last group's value side closes.
+    if (r + 1 < n) {
+      stage(r, R0, R1, R3);
+      if (r + 2 < n) {
+        stage(r + 1, R1, R2, R0);
+        if (r + 3 < n) {
+          stage(r + 2, R2, R3, R1);
+          value_side(R3, s0, s1);
+        } else {
+          value_side(R2, s0, s1);
+        }
+      } else {
+        value_side(R1, s0, s1);
+      }
+    } else {
+      value_side(R0, s0, s1);
+    }
   }
-  for (int r = 0; r + 1 < n; r++) {
-    if (r + 2 < n) load_group(r + 2, Gnn);
-    const float qzn = key_prep(Gn);
-    value_side(G, s0, s1);
-    key_mfma(Gn, qzn, s0, s1);
-    G = Gn;
-    Gn = Gnn;
-  }
-  if (n > 0) value_side(G, s0, s1);
 
   // Wave partial: sums over the four row blocks.
   const float l_tot = wave_sum_rows(l_run);
