@@ -73,14 +73,18 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+PREFILL_CHUNK = 131072
+
+
 def build_caches(torch, kvq, w, copies, max_tokens, dev, gps, ev=None, stream=None):
-    """Build `copies` caches holding the workload's prefill (appends of 16384 tokens).
+    """Build `copies` caches holding the workload's prefill (appends of up to
+    PREFILL_CHUNK tokens per sequence: one append for contexts up to 128K).
     With `ev`, each copy's appends are timed (inputs drawn beforehand) and the
     per-copy prefill times in ms are returned as well."""
     params = wl.torch_key_params(torch, w, dev)
     caches, times = [], []
     lens = w.context_lengths()
-    chunk = 16384
+    chunk = PREFILL_CHUNK
     for c in range(copies):
         cache = kvq.KVCache(w.batch, w.num_q_heads, w.num_kv_heads, bits=w.bits, group=w.group,
                             residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=dev)
@@ -122,7 +126,7 @@ def step_bytes(cache, w):
     return total
 
 
-def cpu_baseline(w, heads=4, steps=3):
+def cpu_baseline(w, heads=4, steps=20):
     """Time the CPU oracle (single BLAS thread) on `heads` KV heads of sequence 0 at
     the workload's full context: per step, append one token and attend."""
     from threadpoolctl import threadpool_limits
@@ -315,7 +319,7 @@ def main():
                "tokens_per_s": round(pf_tokens / (pf_med * 1e-3), 1),
                "input_fp16_gbps": round(pf_in_bytes / (pf_med * 1e-3) / 1e9, 1),
                "in_plus_out_gbps": round((pf_in_bytes + pf_out_per_head * w.num_kv_heads) / (pf_med * 1e-3) / 1e9, 1),
-               "appends_of": 16384, "copies_timed": len(prefill_ms)}
+               "append_tokens_max": PREFILL_CHUNK, "copies_timed": len(prefill_ms)}
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 7919)

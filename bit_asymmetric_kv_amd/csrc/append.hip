@@ -65,123 +65,176 @@ struct QuantOut {
   __half s, z;
 };
 
-// Asymmetric uniform quantization of the values x[0..31] (stride `step`):
-// fp32 range / (2^bits - 1), fp16 scale and zero-point, codes from the stored
-// fp16 scale with round-half-even and a clamp to [0, 2^bits - 1].
+// Token index of value-code slot s held by lane row kb.
+__device__ inline int value_token(int kb, int s) { return s < 4 ? 4 * kb + s : 16 + 4 * kb + (s - 4); }
+
+// Group flush with one wave per group, the data held in registers: the wave reads
+// the group's 32 key rows and 32 value rows (FP16 window or appended input, 16 KB),
+// quantizes keys per channel (lane l: channels 2l and 2l+1 over the 32 tokens) and
+// values per token and 32-channel group (lane l: token l/4 and 16 + l/4, channel
+// group l%4), puts the codes in shared memory and writes the packed block in the
+// MFMA operand order. With rotation, keys read from the input go through the
+// Walsh-Hadamard butterflies across lanes first (fp32 sums and differences, stage by
+// stage as in rotate_rows_to_fp16).
+//
+// Asymmetric uniform quantization of 32 values: fp32 range / (2^bits - 1), fp16
+// scale and zero-point, codes from the stored fp16 scale with round-half-even and a
+// clamp to [0, 2^bits - 1].
 template <int BITS>
-__device__ QuantOut quantize32(const float* x, int step, uint8_t* codes, int cstep) {
+__device__ inline QuantOut quantize_regs(const float* x, uint8_t* codes) {
   const float levels = float((1 << BITS) - 1);
   float mn = x[0], mx = x[0];
   for (int i = 1; i < kG; i++) {
-    float v = x[i * step];
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
   }
-  float s32 = (mx - mn) / levels;
-  __half s16 = __float2half_rn(s32);
-  __half z16 = __float2half_rn(mn);
-  float sf = __half2float(s16);
-  float zf = __half2float(z16);
+  const float s32 = (mx - mn) / levels;
+  const __half s16 = __float2half_rn(s32);
+  const __half z16 = __float2half_rn(mn);
+  const float sf = __half2float(s16);
+  const float zf = __half2float(z16);
   if (sf == 0.0f) {
-    for (int i = 0; i < kG; i++) codes[i * cstep] = 0;
+    for (int i = 0; i < kG; i++) codes[i] = 0;
   } else {
-    float inv = 1.0f / sf;
+    const float inv = 1.0f / sf;
     for (int i = 0; i < kG; i++) {
-      float d = x[i * step] - zf;
+      const float d = x[i] - zf;
       float r = __builtin_rintf(d * inv);
       r = fminf(fmaxf(r, 0.0f), levels);
-      codes[i * cstep] = uint8_t(r);
+      codes[i] = uint8_t(r);
     }
   }
   return {s16, z16};
 }
 
-// Token index of value-code slot s held by lane row kb.
-__device__ inline int value_token(int kb, int s) { return s < 4 ? 4 * kb + s : 16 + 4 * kb + (s - 4); }
-
 template <int BITS>
-__global__ __launch_bounds__(256) void flush_kernel(uint8_t* __restrict__ blocks, const __half* __restrict__ ringk,
-                                                    const __half* __restrict__ ringv, const SeqArgs seq,
-                                                    const __half* __restrict__ kin, const __half* __restrict__ vin,
-                                                    int Hkv, int W, int RS, int sink, long long gcap, int n_max,
-                                                    int rotate) {
+__global__ __launch_bounds__(64) void flush_wave_kernel(uint8_t* __restrict__ blocks,
+                                                        const __half* __restrict__ ringk,
+                                                        const __half* __restrict__ ringv, const SeqArgs seq,
+                                                        const __half* __restrict__ kin,
+                                                        const __half* __restrict__ vin, int Hkv, int W, int RS,
+                                                        int sink, long long gcap, int n_max, int rotate) {
   constexpr int CB = kG * kD * BITS / 8;  // bytes of one code section
   constexpr int GB = 2 * CB + 1024;
-  __shared__ float xk[kG][kD + 1];
-  __shared__ float xv[kG][kD + 1];
-  __shared__ uint8_t ck[kG][kD];
-  __shared__ uint8_t cv[kG][kD];
-  __shared__ int from_input[kG];
+  __shared__ uint8_t ck[kG][kD];  // key codes [token][channel]
+  __shared__ uint8_t cv[kG][kD];  // value codes [token][channel]
+  __shared__ __half vsz[2][kD];   // value scales / zero-points in block order
 
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
   const SeqDesc sd = seq.inl_valid ? seq.inl[b] : seq.dev[b];
   const int nflush = (sd.q_new - sd.q_old) / kG;
   if (int(blockIdx.x) >= nflush) return;
   const int g = sd.q_old / kG + blockIdx.x;
   const int t0 = sink + g * kG;  // with an attention sink, group g starts at token 1 + 32 g
   const size_t bh = size_t(b) * Hkv + h;
-
-  if (threadIdx.x < kG) from_input[threadIdx.x] = (t0 + int(threadIdx.x) >= sd.t_old) ? 1 : 0;
-  for (int e = threadIdx.x; e < kG * kD; e += blockDim.x) {
-    int i = e / kD, d = e % kD;
-    int t = t0 + i;
-    __half kv, vv;
-    if (t < sd.t_old) {
-      size_t off = (bh * RS + size_t(t % W)) * kD + d;
-      kv = ringk[off];
-      vv = ringv[off];
-    } else {
-      size_t off = ((size_t(b) * n_max + (t - sd.t_old)) * Hkv + h) * kD + d;
-      kv = kin[off];
-      vv = vin[off];
-    }
-    xk[i][d] = __half2float(kv);
-    xv[i][d] = __half2float(vv);
-  }
-  __syncthreads();
-  if (rotate) rotate_rows_to_fp16(&xk[0][0], kD + 1, kG, from_input);
-
-  __shared__ __half ks[kD], kz[kD], vs[kD], vz[kD];
-  if (threadIdx.x < kD) {
-    int d = threadIdx.x;  // keys: one channel over the group's 32 tokens
-    QuantOut r = quantize32<BITS>(&xk[0][d], kD + 1, &ck[0][d], kD);
-    ks[d] = r.s;
-    kz[d] = r.z;
-  } else {
-    int idx = threadIdx.x - kD;  // values: one token, one 32-channel group
-    int i = idx / 4, j = idx % 4;
-    QuantOut r = quantize32<BITS>(&xv[i][j * kG], 1, &cv[i][j * kG], 1);
-    int kb = (i % 16) / 4, s = 4 * (i / 16) + i % 4;
-    int vi = (kb * 4 + j) * 8 + s;
-    vs[vi] = r.s;
-    vz[vi] = r.z;
-  }
-  __syncthreads();
-
+  // Row of token t: FP16 window slot t % W if it was appended before, else input row.
+  auto row = [&](const __half* ring, const __half* in, int t) -> const __half* {
+    return t < sd.t_old ? ring + (bh * RS + size_t(t % W)) * kD
+                        : in + ((size_t(b) * n_max + (t - sd.t_old)) * Hkv + h) * kD;
+  };
   uint8_t* blk = blocks + (bh * size_t(gcap) + g) * GB;
+
+  // Every load of the group is issued before any arithmetic: 32 key words (channels
+  // 2l, 2l+1 of each token) and the lane's two 64-byte value segments.
+  uint32_t ku[kG];
+  for (int i = 0; i < kG; i++) ku[i] = *reinterpret_cast<const uint32_t*>(row(ringk, kin, t0 + i) + 2 * lane);
+  uint4 vu[2][4];
+  for (int k = 0; k < 2; k++) {
+    const uint4* src = reinterpret_cast<const uint4*>(row(ringv, vin, t0 + 16 * k + lane / 4) + kG * (lane % 4));
+    for (int q = 0; q < 4; q++) vu[k][q] = src[q];
+  }
+
+  // Keys.
+  {
+    float x0[kG], x1[kG];
+    for (int i = 0; i < kG; i++) {
+      x0[i] = __half2float(__ushort_as_half(static_cast<unsigned short>(ku[i] & 0xFFFFu)));
+      x1[i] = __half2float(__ushort_as_half(static_cast<unsigned short>(ku[i] >> 16)));
+    }
+    if (rotate) {
+      for (int i = 0; i < kG; i++) {
+        if (t0 + i < sd.t_old) continue;  // window rows are stored rotated already
+        float a = x0[i], c = x1[i];
+        float p0 = a + c, p1 = a - c;  // half-width 1: channels 2l, 2l + 1
+        for (int m = 1; m < kD / 2; m <<= 1) {  // half-width 2m: partner lane l ^ m
+          const float q0 = __shfl_xor(p0, m), q1 = __shfl_xor(p1, m);
+          if ((lane & m) == 0) {
+            p0 = p0 + q0;
+            p1 = p1 + q1;
+          } else {
+            p0 = q0 - p0;
+            p1 = q1 - p1;
+          }
+        }
+        float y0 = p0 * kInvSqrt128, y1 = p1 * kInvSqrt128;
+        asm volatile("" : "+v"(y0), "+v"(y1));  // round the product to fp32 first
+        x0[i] = __half2float(__float2half_rn(y0));
+        x1[i] = __half2float(__float2half_rn(y1));
+      }
+    }
+    uint8_t c0[kG], c1[kG];
+    const QuantOut r0 = quantize_regs<BITS>(x0, c0);
+    const QuantOut r1 = quantize_regs<BITS>(x1, c1);
+    for (int i = 0; i < kG; i++)
+      *reinterpret_cast<uint16_t*>(&ck[i][2 * lane]) = uint16_t(c0[i]) | uint16_t(c1[i]) << 8;
+    uint32_t* sz = reinterpret_cast<uint32_t*>(blk + 2 * CB);
+    sz[lane] = uint32_t(__half_as_ushort(r0.s)) | uint32_t(__half_as_ushort(r1.s)) << 16;
+    sz[kD / 2 + lane] = uint32_t(__half_as_ushort(r0.z)) | uint32_t(__half_as_ushort(r1.z)) << 16;
+  }
+  // Values.
+  for (int k = 0; k < 2; k++) {
+    const int i = 16 * k + lane / 4, j = lane % 4;
+    float x[kG];
+    for (int q = 0; q < 4; q++) {
+      const uint4 u = vu[k][q];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      for (int e = 0; e < 4; e++) {
+        x[8 * q + 2 * e] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[e] & 0xFFFFu)));
+        x[8 * q + 2 * e + 1] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[e] >> 16)));
+      }
+    }
+    uint8_t c[kG];
+    const QuantOut r = quantize_regs<BITS>(x, c);
+    uint32_t wds[kG / 4];
+    for (int q = 0; q < kG / 4; q++)
+      wds[q] = uint32_t(c[4 * q]) | uint32_t(c[4 * q + 1]) << 8 | uint32_t(c[4 * q + 2]) << 16 |
+               uint32_t(c[4 * q + 3]) << 24;
+    uint4* dst = reinterpret_cast<uint4*>(&cv[i][kG * j]);
+    dst[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+    dst[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
+    const int kb = (i % 16) / 4, sl = 4 * (i / 16) + i % 4;
+    const int vi = (kb * 4 + j) * 8 + sl;
+    vsz[0][vi] = r.s;
+    vsz[1][vi] = r.z;
+  }
+  __syncthreads();
+
+  // Packed words: key token i, channel d is slot d%8 of operand 2(d/32) + i/16 in
+  // lane i%16 + 16((d%32)/8); value token i, channel d is slot 4(i/16) + i%4 of
+  // operand d/16 in lane d%16 + 16((i%16)/4).
   uint32_t* kw = reinterpret_cast<uint32_t*>(blk);
   uint32_t* vw = reinterpret_cast<uint32_t*>(blk + CB);
   constexpr int NW = CB / 4;
-  for (int w = threadIdx.x; w < NW; w += blockDim.x) {
+  for (int w = lane; w < NW; w += 64) {
     uint32_t kword = 0, vword = 0;
     if (BITS == 2) {
-      int l = w / 4, ohi = w % 4;
+      const int l = w / 4, ohi = w % 4;
       for (int par = 0; par < 2; par++) {
-        int o = 2 * ohi + par;
-        for (int s = 0; s < 8; s++) {
-          int bit = 8 * (s / 2) + 4 * (s % 2) + 2 * par;
-          int ki = 16 * (o % 2) + l % 16, kd = 32 * (o / 2) + 8 * (l / 16) + s;
-          int vd = 16 * o + l % 16, vi = value_token(l / 16, s);
+        const int o = 2 * ohi + par;
+        for (int s2 = 0; s2 < 8; s2++) {
+          const int bit = 8 * (s2 / 2) + 4 * (s2 % 2) + 2 * par;
+          const int ki = 16 * (o % 2) + l % 16, kd = 32 * (o / 2) + 8 * (l / 16) + s2;
+          const int vd = 16 * o + l % 16, vi = value_token(l / 16, s2);
           kword |= uint32_t(ck[ki][kd]) << bit;
           vword |= uint32_t(cv[vi][vd]) << bit;
         }
       }
     } else {
-      int o = 4 * (w / 256) + w % 4, l = (w % 256) / 4;
-      for (int s = 0; s < 8; s++) {
-        int bit = 8 * (s % 4) + 4 * (s / 4);
-        int ki = 16 * (o % 2) + l % 16, kd = 32 * (o / 2) + 8 * (l / 16) + s;
-        int vd = 16 * o + l % 16, vi = value_token(l / 16, s);
+      const int o = 4 * (w / 256) + w % 4, l = (w % 256) / 4;
+      for (int s2 = 0; s2 < 8; s2++) {
+        const int bit = 8 * (s2 % 4) + 4 * (s2 / 4);
+        const int ki = 16 * (o % 2) + l % 16, kd = 32 * (o / 2) + 8 * (l / 16) + s2;
+        const int vd = 16 * o + l % 16, vi = value_token(l / 16, s2);
         kword |= uint32_t(ck[ki][kd]) << bit;
         vword |= uint32_t(cv[vi][vd]) << bit;
       }
@@ -189,14 +242,10 @@ __global__ __launch_bounds__(256) void flush_kernel(uint8_t* __restrict__ blocks
     kw[w] = kword;
     vw[w] = vword;
   }
-  __half* sz = reinterpret_cast<__half*>(blk + 2 * CB);
-  if (threadIdx.x < kD) {
-    int d = threadIdx.x;
-    sz[d] = ks[d];
-    sz[kD + d] = kz[d];
-    sz[2 * kD + d] = vs[d];
-    sz[3 * kD + d] = vz[d];
-  }
+  uint32_t* vszw = reinterpret_cast<uint32_t*>(blk + 2 * CB + 512);
+  const uint32_t* vszl = reinterpret_cast<const uint32_t*>(&vsz[0][0]);
+  vszw[lane] = vszl[lane];
+  vszw[64 + lane] = vszl[64 + lane];
 }
 
 // One block per (appended token that stays in FP16, kv-head, sequence). Window
@@ -243,10 +292,10 @@ hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqArgs& seq, cons
   auto* kin = static_cast<const __half*>(k);
   auto* vin = static_cast<const __half*>(v);
   if (L.bits == 2)
-    hipLaunchKernelGGL(flush_kernel<2>, grid, dim3(256), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
+    hipLaunchKernelGGL(flush_wave_kernel<2>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
                        L.RS, L.sink, (long long)L.gcap, n_max, rotate);
   else
-    hipLaunchKernelGGL(flush_kernel<4>, grid, dim3(256), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
+    hipLaunchKernelGGL(flush_wave_kernel<4>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
                        L.RS, L.sink, (long long)L.gcap, n_max, rotate);
   return hipGetLastError();
 }
