@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-CHUNK = 16384
+CHUNK = 131072  # prefill append size, as bench.py appends
 
 
 @pytest.fixture(scope="module")
