@@ -14,6 +14,7 @@ from .kvq_oracle import (  # noqa: F401
     dequantize_block,
     quantized_count,
     attention_fp64,
+    rope_fp64,
     OracleHead,
     OracleCache,
     group_block_bytes,

@@ -34,12 +34,27 @@ def simulate_quantized_count(T: int, R: int, G: int, sink: bool = False) -> int:
     return q
 
 
+def rotate_pairs_scalar(key, t, base):
+    """Rotary embedding of one key row at position t, one channel pair at a time:
+    channels f and f + D/2 turn by the angle t * base^(-2f / D)."""
+    D = len(key)
+    half = D // 2
+    out = [0.0] * D
+    for f in range(half):
+        ang = t * math.pow(base, -2.0 * f / D)
+        c, s = math.cos(ang), math.sin(ang)
+        out[f] = key[f] * c - key[f + half] * s
+        out[f + half] = key[f + half] * c + key[f] * s
+    return out
+
+
 def dense_decode(q_rows, k16, v16, head, scale=None):
     """Attention of q_rows [H, D] over a whole sequence held by `head`.
 
     `head` supplies per-group quantization results (its kc/ks/kz/vc/vs/vz
     arrays) and the FP16 history k16/v16 [T, D]; this function decides per token
-    which representation attention uses and dequantizes scalar by scalar.
+    which representation attention uses and dequantizes scalar by scalar. With
+    `head.rope`, every key (dequantized or FP16) is then rotated at its position.
     """
     T, D = k16.shape
     G = head.G
@@ -60,6 +75,8 @@ def dense_decode(q_rows, k16, v16, head, scale=None):
         else:
             keys[t] = k16[t].astype(np.float64)
             vals[t] = v16[t].astype(np.float64)
+        if getattr(head, "rope", False):
+            keys[t] = rotate_pairs_scalar([float(x) for x in keys[t]], t, head.rope_base)
     out = np.zeros((q_rows.shape[0], D))
     for h in range(q_rows.shape[0]):
         scores = np.array([sum(float(q_rows[h, d]) * keys[t, d] for d in range(D)) * scale

@@ -25,6 +25,11 @@ What it computes, in the pages' order:
   ("KV cache quantization ...", full-text-skim notes on KIVI's grouped/residual split).
 * Decode attention: standard scaled dot-product softmax attention over every cached
   token, computed here in float64 on the dequantized cache.
+* Pre-RoPE keys (optional): keys are quantized before the rotary position
+  embedding and the rotation is applied after dequantization, at each key's
+  position ("KVQuant" review, Method and Key idea: quantize keys per channel
+  before RoPE, apply RoPE after dequantization; Prior limitations: RoPE rotates
+  and mixes channel pairs, smearing the outlier channels).
 
 Readings where the pages are silent (each is listed with its reason in the design
 notes of the repository):
@@ -40,7 +45,12 @@ notes of the repository):
   fp32(1/sqrt(128)); rotated k rounded to fp16 before it is stored or quantized;
   rotated q kept in fp32; v is not rotated;
 * softmax scale 1/sqrt(head_dim) unless given; query head hq reads KV head
-  hq // (Hq // Hkv).
+  hq // (Hq // Hkv);
+* RoPE (the pages do not define it; the standard rotary embedding is taken): the
+  channel pairs (f, f + 64), f = 0..63, of a key at position t (its 0-based index
+  in the sequence) are rotated by the angle t * theta_f, theta_f = base^(-f / 64),
+  base 10000 unless given: (a, b) -> (a cos - b sin, b cos + a sin); the query is
+  passed already rotated at its own position, so attention reads q . RoPE_t(k).
 
 The packed layout of one group block is this library's own storage format (the
 pages only ask for a fixed per-token bit count); it is restated here from its
@@ -299,6 +309,23 @@ def quantized_count(T: int, R: int, G: int = GROUP, sink: bool = False) -> int:
     return G * (max(0, T - o - R) // G)
 
 
+ROPE_BASE = 10000.0
+
+
+def rope_fp64(x: np.ndarray, positions, base: float = ROPE_BASE) -> np.ndarray:
+    """Rotary position embedding of rows x [n, 128] at integer positions [n], in
+    float64: channel f and channel f + 64 form a pair rotated by position * theta_f
+    with theta_f = base^(-f / 64) (the standard rotary embedding, pairs taken as the
+    two halves of the head; see the module notes)."""
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
+    theta = float(base) ** (-np.arange(half, dtype=np.float64) / half)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[:, :half], x[:, half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=1)
+
+
 def attention_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
     """Softmax attention of query rows q [H, D] over keys/values [T, D], float64."""
     q = np.asarray(q, dtype=np.float64)
@@ -317,12 +344,19 @@ class OracleHead:
     With `sink`, token 0 is an attention sink: it stays FP16 for good and the
     groups cover tokens [1 + g G, 1 + (g + 1) G) ("KV cache quantization: putting
     the bits in the cached vectors", full-text-skim notes: keeping the first token
-    in fp16 helps, most at 2 bits)."""
+    in fp16 helps, most at 2 bits).
+
+    With `rope`, the appended keys are pre-RoPE: they are stored and quantized as
+    given, and attention rotates every key, dequantized or FP16, at its position
+    ("KVQuant" review, Method and Key idea)."""
 
     def __init__(self, bits: int, residual: int, rotate: bool = False,
-                 head_dim: int = HEAD_DIM, group: int = GROUP, sink: bool = False):
+                 head_dim: int = HEAD_DIM, group: int = GROUP, sink: bool = False,
+                 rope: bool = False, rope_base: float = ROPE_BASE):
         if head_dim != HEAD_DIM or group != GROUP:
             raise ValueError("oracle block format is defined for head_dim 128, G 32")
+        if rope and rotate:
+            raise ValueError("pre-RoPE keys and the Walsh-Hadamard rotation are exclusive")
         if residual < 0 or residual % group:
             raise ValueError("residual must be a non-negative multiple of G")
         self.bits = bits
@@ -331,6 +365,8 @@ class OracleHead:
         self.rotate = bool(rotate)
         self.sink = bool(sink)
         self.o = 1 if sink else 0   # first token of group 0
+        self.rope = bool(rope)
+        self.rope_base = float(rope_base)
         self.k16 = np.zeros((0, head_dim), dtype=_F16)   # every appended key (rotated if asked)
         self.v16 = np.zeros((0, head_dim), dtype=_F16)
         nv = head_dim // group
@@ -401,11 +437,15 @@ class OracleHead:
         v_hat = vz_full + vs_full * self.vc.astype(np.float64)
         k_tail = self.k16[self.o + self.Q:].astype(np.float64)
         v_tail = self.v16[self.o + self.Q:].astype(np.float64)
+        pos = np.arange(self.o, self.T)          # quantized tokens, then the window
         if self.sink and self.T > 0:
             k_tail = np.concatenate([k_tail, self.k16[:1].astype(np.float64)], axis=0)
             v_tail = np.concatenate([v_tail, self.v16[:1].astype(np.float64)], axis=0)
+            pos = np.concatenate([pos, [0]])
         k_all = np.concatenate([k_hat.reshape(ng * self.G, HEAD_DIM), k_tail], axis=0)
         v_all = np.concatenate([v_hat.reshape(ng * self.G, HEAD_DIM), v_tail], axis=0)
+        if self.rope:
+            k_all = rope_fp64(k_all, pos, self.rope_base)
         return k_all, v_all
 
     def prepare_query(self, q: np.ndarray) -> np.ndarray:
@@ -429,14 +469,15 @@ class OracleCache:
     """Batch of sequences x kv-heads, mirroring the library's cache object."""
 
     def __init__(self, batch, num_q_heads, num_kv_heads, bits, residual,
-                 rotate=False, softmax_scale=None, head_dim=HEAD_DIM, group=GROUP, sink=False):
+                 rotate=False, softmax_scale=None, head_dim=HEAD_DIM, group=GROUP, sink=False,
+                 rope=False, rope_base=ROPE_BASE):
         if num_q_heads % num_kv_heads:
             raise ValueError("num_q_heads must be a multiple of num_kv_heads")
         self.B = batch
         self.Hq = num_q_heads
         self.Hkv = num_kv_heads
         self.scale = softmax_scale if softmax_scale else 1.0 / math.sqrt(head_dim)
-        self.heads = [[OracleHead(bits, residual, rotate, head_dim, group, sink)
+        self.heads = [[OracleHead(bits, residual, rotate, head_dim, group, sink, rope, rope_base)
                        for _ in range(num_kv_heads)] for _ in range(batch)]
 
     def append(self, k, v, n_tokens=None):
