@@ -87,7 +87,8 @@ def build_caches(torch, kvq, w, copies, max_tokens, dev, gps, ev=None, stream=No
     chunk = PREFILL_CHUNK
     for c in range(copies):
         cache = kvq.KVCache(w.batch, w.num_q_heads, w.num_kv_heads, bits=w.bits, group=w.group,
-                            residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=dev)
+                            residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=dev,
+                            sink=w.sink, rope=w.rope)
         if gps:
             cache.set_decode_split(gps)
         gen = torch.Generator(device=dev)
@@ -136,7 +137,7 @@ def cpu_baseline(w, heads=4, steps=20):
     with threadpool_limits(1):
         hs = []
         for h in range(heads):
-            oh = OracleHead(w.bits, w.residual, w.rotate)
+            oh = OracleHead(w.bits, w.residual, w.rotate, sink=w.sink, rope=w.rope)
             oh.append(wl.keys(w, 0, h, 0, T0), wl.values(w, 0, h, 0, T0))
             hs.append(oh)
         nbytes = 0

@@ -47,6 +47,8 @@ class KVQConfig(ctypes.Structure):
         ("max_tokens", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float),
         ("sink", ctypes.c_int32),
+        ("rope", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
     ]
 
 
@@ -113,11 +115,12 @@ def check(status: int) -> None:
 
 
 def make_config(batch, num_q_heads, num_kv_heads, head_dim=128, bits=2, group=32, residual=128,
-                rotate=False, max_tokens=4096, softmax_scale=0.0, sink=False) -> KVQConfig:
+                rotate=False, max_tokens=4096, softmax_scale=0.0, sink=False, rope=False,
+                rope_base=0.0) -> KVQConfig:
     def flag(x):
         return int(bool(x)) if x in (True, False) else int(x)
     return KVQConfig(batch, num_q_heads, num_kv_heads, head_dim, bits, group, residual, flag(rotate),
-                     max_tokens, softmax_scale, flag(sink))
+                     max_tokens, softmax_scale, flag(sink), flag(rope), rope_base)
 
 
 def cache_bytes(cfg: KVQConfig) -> int:
@@ -138,11 +141,12 @@ class KVCache:
     """A low-bit KV cache on one GPU, owning its device memory as a torch tensor."""
 
     def __init__(self, batch, num_q_heads, num_kv_heads, head_dim=128, bits=2, group=32, residual=128,
-                 rotate=False, max_tokens=4096, softmax_scale=0.0, device="cuda", sink=False):
+                 rotate=False, max_tokens=4096, softmax_scale=0.0, device="cuda", sink=False, rope=False,
+                 rope_base=0.0):
         import torch
         self._torch = torch
         self.cfg = make_config(batch, num_q_heads, num_kv_heads, head_dim, bits, group, residual,
-                               rotate, max_tokens, softmax_scale, sink)
+                               rotate, max_tokens, softmax_scale, sink, rope, rope_base)
         self.device = torch.device(device)
         nbytes = cache_bytes(self.cfg)
         self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)

@@ -53,6 +53,11 @@ struct DecodeArgs {
   SplitPlan plan;  // split workgroups per sequence and the partial slots per query head
   AppendArgs app;  // an append folded into this launch (app.pending)
   float scale_log2;
+  // Pre-RoPE keys: cos / sin of the rotary angles at every group start position
+  // o + 32 g ([g][cos 64 | sin 64] fp32) and at the in-group offsets i = 0..31
+  // ([i][cos 64 | sin 64]); null without RoPE.
+  const float* rope_tab;
+  const float* rope_in;
 };
 
 // 8 two-bit codes of one MFMA operand: `m` holds them in bits 0-1 and 4-5 of each
@@ -251,9 +256,13 @@ __device__ void merge_and_store(const DecodeArgs& a, int b, int h, int split, co
 // channels 2l and 2l + 1 over the chunk's tokens.
 // With an append folded into the launch (caches without rotation), tokens
 // t >= t_old come from the appended rows and are written to the ring.
-template <int HG>
+// With pre-RoPE keys (ROPE), the keys of a chunk starting at a group start position
+// (rope_entry >= 0: the position's entry in a.rope_tab) are rotated after loading:
+// lane l pairs its channel with the same token's channel 64 away, held by lane l^32.
+template <int HG, bool ROPE>
 __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt, int s0, int wlim, int t_old,
-                             const float (*qf)[kD], const float* expo, const WaveParts& wp, int wave, int lane) {
+                             const float (*qf)[kD], const float* expo, const WaveParts& wp, int wave, int lane,
+                             int rope_entry, const float* ropein) {
   if (cnt <= 0) {
     if (lane < HG) {
       wp.at(wave, lane, 0) = -INFINITY;
@@ -292,6 +301,19 @@ __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt,
   for (int i = 0; i < 8; i++) {
     const half8 k8 = __builtin_bit_cast(half8, kr[i]);
     for (int e = 0; e < 8; e++) kf[8 * i + e] = float(k8[e]);
+  }
+  if constexpr (ROPE) {
+    if (rope_entry >= 0) {
+      // angle (t0 + tl) theta_f = base angle of t0 plus in-group angle of tl
+      const float* bt = a.rope_tab + size_t(rope_entry) * kD;
+      const float* it = ropein + tl * kD;
+      for (int d = 0; d < 64; d++) {
+        const float xp = __shfl_xor(kf[d], 32);
+        const float c = bt[d] * it[d] - bt[64 + d] * it[64 + d];
+        const float sn = bt[64 + d] * it[d] + bt[d] * it[64 + d];
+        kf[d] = hf == 0 ? kf[d] * c - xp * sn : kf[d] * c + xp * sn;
+      }
+    }
   }
   if (pend && t0 + cnt > t_old) {
     // Appended tokens in this chunk: write their keys and values to the ring.
@@ -348,7 +370,7 @@ struct GroupRegs {
   half8 vs[NJ], vz[NJ];      // value scale / zero of this lane's 8 tokens per channel group
 };
 
-template <int BITS, int HG>
+template <int BITS, int HG, bool ROPE>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // MFMA columns. Key side: U = 2 * HG column kinds, the fp16 high part of head u at
   // u < HG and the low part of head U - 1 - u at u >= HG (u = column % U), repeated
@@ -372,6 +394,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       half8 b[4][4][U];
     } bk[kWaves];
   } sh;
+  // Pre-RoPE keys: in-group rotary cos / sin [32][128], and per wave the current
+  // group's key scales / zero-points (512 B) and base-angle cos / sin (512 B).
+  __shared__ float ropein[ROPE ? kG * kD : 1];
+  __shared__ uint4 ropew[ROPE ? kWaves * 64 : 1];
   const WaveParts wp{wpart_mem, HG * kPartialStride};
 
   // 1-D grid: the split workgroups first, sequence by sequence in the plan's order
@@ -435,8 +461,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       G.kc1 = *reinterpret_cast<const uint4*>(blk + 1024 + 16 * lane);
       G.vc1 = *reinterpret_cast<const uint4*>(blk + CB + 1024 + 16 * lane);
     }
-    G.ks = load_half8(blk + 2 * CB + 16 * (lane / 4));
-    G.kz = load_half8(blk + 2 * CB + 256 + 16 * (lane / 4));
+    if constexpr (ROPE) {
+      // lanes 0-31: the key scale / zero-point region; lanes 32-63: the rotary
+      // cos / sin of the group's start position
+      G.ks = lane < 32 ? load_half8(blk + 2 * CB + 16 * lane)
+                       : load_half8(reinterpret_cast<const uint8_t*>(a.rope_tab + size_t(wg0 + r) * kD) +
+                                    16 * (lane - 32));
+    } else {
+      G.ks = load_half8(blk + 2 * CB + 16 * (lane / 4));
+      G.kz = load_half8(blk + 2 * CB + 256 + 16 * (lane / 4));
+    }
     const int kb_ = lane / 16, col_ = lane % 16, u_ = col_ % (2 * HG);
     const int kcopy_ = 2 * (col_ / (2 * HG)) + (u_ < HG ? 0 : 1);
     const int jbase_ = (kcopy_ % (4 / NJ)) * NJ;
@@ -454,6 +488,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     load_group(min(2, n - 1), R2);
   }
 
+  if constexpr (ROPE) {
+    for (int e = threadIdx.x; e < kG * kD / 4; e += blockDim.x)
+      reinterpret_cast<float4*>(ropein)[e] = reinterpret_cast<const float4*>(a.rope_in)[e];
+    __syncthreads();
+  }
+
   // The FP16-window workgroup and rotated queries use the shared-memory query
   // preparation; otherwise each wave prepares what its lanes need on its own.
   if (tail || a.rotate) prepare_query<HG>(a, b, h, qf, expo);
@@ -464,11 +504,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     // [o + Q + 32 (c - 1), ...) of the window; without one, chunk c holds
     // [Q + 32 c, ...). Window token t is in ring slot t % W.
     const int chunk = (split - nsb) * kWaves + wave;
-    if (a.sink && chunk == 0) {
-      window_chunk<HG>(a, b, h, 0, min(1, T), a.W, a.W + 1, sd.t_old, qf, expo, wp, wave, lane);
+    if (a.sink && chunk == 0) {  // position 0: no rotation
+      window_chunk<HG, ROPE>(a, b, h, 0, min(1, T), a.W, a.W + 1, sd.t_old, qf, expo, wp, wave, lane, -1, ropein);
     } else {
-      const int t0 = a.sink + Q + (chunk - a.sink) * kG;
-      window_chunk<HG>(a, b, h, t0, min(kG, T - t0), t0 % a.W, a.W, sd.t_old, qf, expo, wp, wave, lane);
+      const int t0 = a.sink + Q + (chunk - a.sink) * kG;  // start of group Q / 32 + chunk - sink
+      window_chunk<HG, ROPE>(a, b, h, t0, min(kG, T - t0), t0 % a.W, a.W, sd.t_old, qf, expo, wp, wave, lane,
+                             Q / kG + chunk - a.sink, ropein);
     }
     // A folded append with inline records: store them as the sequence's state.
     if (a.app.pending && a.app.seq.inl_valid && h == 0 && split == nsb && threadIdx.x == 0)
@@ -580,6 +621,66 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
+  // Pre-RoPE keys: scores of the group's 32 tokens from the dequantized keys
+  // z + s * c rotated at their positions. Lane (token i, k-block kb) holds channels
+  // 32 kc + 8 kb + slot for kc = 0..3, so the rotary pair (f, f + 64) of its channel
+  // f < 64 sits in operand kc + 2 of the same lane and slot. The rotated key is
+  // split into fp16 high and low parts, two MFMAs each against B = q (high / low
+  // columns, staged once). The group's scale / zero-point region and its start
+  // angle's cos / sin come through this wave's shared memory; the in-group angle
+  // from the workgroup's table.
+  auto key_rope = [&](const GroupRegs<BITS, NJ>& g, float4v& r0, float4v& r1) {
+    uint4* wl = ropew + wave * 64;
+    wl[lane] = __builtin_bit_cast(uint4, g.ks);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint8_t* wb = reinterpret_cast<const uint8_t*>(wl);
+    const float* bcs = reinterpret_cast<const float*>(wb + 512);  // cos[64] | sin[64] of the start
+    r0 = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    r1 = r0;
+    for (int kc = 0; kc < 2; kc++) {
+      const half8 sa = *reinterpret_cast<const half8*>(wb + 64 * kc + 16 * kb);
+      const half8 za = *reinterpret_cast<const half8*>(wb + 256 + 64 * kc + 16 * kb);
+      const half8 sb = *reinterpret_cast<const half8*>(wb + 64 * (kc + 2) + 16 * kb);
+      const half8 zb = *reinterpret_cast<const half8*>(wb + 256 + 64 * (kc + 2) + 16 * kb);
+      const int f0 = 32 * kc + 8 * kb;  // frequency of slot 0
+      const half8 bka = sh.bk[wave].b[kc][kb][(u + (U / 2) * kb) % U];
+      const half8 bkb = sh.bk[wave].b[kc + 2][kb][(u + (U / 2) * kb) % U];
+      for (int tile = 0; tile < 2; tile++) {
+        const float* it = ropein + (16 * tile + lane % 16) * kD;
+        const half8 ca = code_operand<BITS>(g.kc0, g.kc1, 2 * kc + tile);
+        const half8 cb = code_operand<BITS>(g.kc0, g.kc1, 2 * (kc + 2) + tile);
+        half8 ah, al, bh, bl;
+        for (int s2 = 0; s2 < 8; s2++) {
+          const float bc = bcs[f0 + s2], bs = bcs[64 + f0 + s2];
+          const float ci = it[f0 + s2], si = it[64 + f0 + s2];
+          const float c = bc * ci - bs * si;
+          const float sn = bs * ci + bc * si;
+          const float xa = __builtin_fmaf(float(ca[s2]), float(sa[s2]), float(za[s2]));
+          const float xb = __builtin_fmaf(float(cb[s2]), float(sb[s2]), float(zb[s2]));
+          const float ya = xa * c - xb * sn;
+          const float yb = xb * c + xa * sn;
+          ah[s2] = _Float16(ya);
+          al[s2] = _Float16(ya - float(ah[s2]));
+          bh[s2] = _Float16(yb);
+          bl[s2] = _Float16(yb - float(bh[s2]));
+        }
+        float4v r = tile == 0 ? r0 : r1;
+        r = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bka, r, 0, 0, 0);
+        r = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bka, r, 0, 0, 0);
+        r = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh, bkb, r, 0, 0, 0);
+        r = __builtin_amdgcn_mfma_f32_16x16x32_f16(bl, bkb, r, 0, 0, 0);
+        if (tile == 0) r0 = r;
+        else r1 = r;
+      }
+    }
+    for (int i = 0; i < 4; i++) {
+      r0[i] += partner<U>(r0[i]);
+      r1[i] += partner<U>(r1[i]);
+    }
+  };
+
   auto value_side = [&](const GroupRegs<BITS, NJ>& g, const float4v& r0, const float4v& r1) {
     const float sc[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
     // Online softmax. Scores stay in the prescaled units S (log2 units are ex * S);
@@ -625,12 +726,27 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   auto stage = [&](int r, const GroupRegs<BITS, NJ>& Gr, const GroupRegs<BITS, NJ>& Gr1,
                    GroupRegs<BITS, NJ>& Gr3) {
     load_group(min(r + 3, n - 1), Gr3);
-    const float qzn = key_prep(Gr1);
-    value_side(Gr, s0, s1);
-    key_mfma(Gr1, qzn, s0, s1);
+    if constexpr (ROPE) {
+      value_side(Gr, s0, s1);
+      key_rope(Gr1, s0, s1);
+    } else {
+      const float qzn = key_prep(Gr1);
+      value_side(Gr, s0, s1);
+      key_mfma(Gr1, qzn, s0, s1);
+    }
   };
+  if constexpr (ROPE) {
+    // B = q for every group: the high / low split of q times a unit scale.
+    GroupRegs<BITS, NJ> unit;
+    for (int e = 0; e < 8; e++) {
+      unit.ks[e] = _Float16(1.0f);
+      unit.kz[e] = _Float16(0.0f);
+    }
+    (void)key_prep(unit);
+  }
   if (n > 0) {
-    key_mfma(R0, key_prep(R0), s0, s1);
+    if constexpr (ROPE) key_rope(R0, s0, s1);
+    else key_mfma(R0, key_prep(R0), s0, s1);
     int r = 0;
     for (; r + 4 < n; r += 4) {
       stage(r, R0, R1, R3);
@@ -734,11 +850,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   }
 }
 
-template <int BITS, int HG>
+template <int BITS, int HG, bool ROPE>
 int resident_blocks_of() {
   int dev = 0, per_cu = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<BITS, HG>, 256, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<BITS, HG, ROPE>, 256, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
@@ -746,21 +862,67 @@ int resident_blocks_of() {
   return per_cu * cus;
 }
 
-template <int BITS, int HG>
+template <int BITS, int HG, bool ROPE>
 hipError_t launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
   const int nsplit_total = a.plan.use_prefix ? a.plan.prefix[B] : B * a.plan.uniform;
-  hipLaunchKernelGGL((decode_split_kernel<BITS, HG>), dim3((nsplit_total + B * a.wblocks) * a.Hkv), dim3(256), 0,
+  hipLaunchKernelGGL((decode_split_kernel<BITS, HG, ROPE>), dim3((nsplit_total + B * a.wblocks) * a.Hkv), dim3(256), 0,
                      stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int decode_resident_blocks(int bits, int hg) {
-  if (bits == 2) return hg == 1 ? resident_blocks_of<2, 1>() : hg == 2 ? resident_blocks_of<2, 2>()
-                      : hg == 4 ? resident_blocks_of<2, 4>() : resident_blocks_of<2, 8>();
-  return hg == 1 ? resident_blocks_of<4, 1>() : hg == 2 ? resident_blocks_of<4, 2>()
-         : hg == 4 ? resident_blocks_of<4, 4>() : resident_blocks_of<4, 8>();
+// Rotary cos / sin tables of a pre-RoPE cache, computed once in fp64 and stored in
+// fp32: entry g holds cos(p theta_f), sin(p theta_f) at the group start position
+// p = o + 32 g, and the in-group table holds them at p = i, i = 0..31, with
+// theta_f = base^(-f / 64), f = 0..63 (the standard rotary embedding over the
+// channel pairs f, f + 64).
+__global__ void rope_table_kernel(float* __restrict__ tab, float* __restrict__ in_tab, int entries, int o,
+                                  double base) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int f = idx % 64;
+  const double theta = pow(base, -double(f) / 64.0);
+  if (idx < entries * 64) {
+    const int g = idx / 64;
+    const double ang = double(o + kG * g) * theta;
+    tab[size_t(g) * kD + f] = float(cos(ang));
+    tab[size_t(g) * kD + 64 + f] = float(sin(ang));
+  } else if (idx < entries * 64 + kG * 64) {
+    const int i = (idx - entries * 64) / 64;
+    const double ang = double(i) * theta;
+    in_tab[i * kD + f] = float(cos(ang));
+    in_tab[i * kD + 64 + f] = float(sin(ang));
+  }
+}
+
+hipError_t launch_rope_tables(const Layout& L, uint8_t* base, double rope_base, hipStream_t stream) {
+  const int total = L.rope_entries * 64 + kG * 64;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((total + 255) / 256), dim3(256), 0, stream,
+                     reinterpret_cast<float*>(base + L.rope_off), reinterpret_cast<float*>(base + L.ropein_off),
+                     L.rope_entries, L.sink, rope_base);
+  return hipGetLastError();
+}
+
+template <bool ROPE>
+int resident_blocks_for(int bits, int hg) {
+  if (bits == 2)
+    return hg == 1 ? resident_blocks_of<2, 1, ROPE>() : hg == 2 ? resident_blocks_of<2, 2, ROPE>()
+           : hg == 4 ? resident_blocks_of<2, 4, ROPE>() : resident_blocks_of<2, 8, ROPE>();
+  return hg == 1 ? resident_blocks_of<4, 1, ROPE>() : hg == 2 ? resident_blocks_of<4, 2, ROPE>()
+         : hg == 4 ? resident_blocks_of<4, 4, ROPE>() : resident_blocks_of<4, 8, ROPE>();
+}
+
+int decode_resident_blocks(int bits, int hg, int rope) {
+  return rope ? resident_blocks_for<true>(bits, hg) : resident_blocks_for<false>(bits, hg);
+}
+
+template <bool ROPE>
+hipError_t launch_split_for(const DecodeArgs& a, int bits, int hg, int B, hipStream_t stream) {
+  if (bits == 2)
+    return hg == 1 ? launch_split<2, 1, ROPE>(a, B, stream) : hg == 2 ? launch_split<2, 2, ROPE>(a, B, stream)
+           : hg == 4 ? launch_split<2, 4, ROPE>(a, B, stream) : launch_split<2, 8, ROPE>(a, B, stream);
+  return hg == 1 ? launch_split<4, 1, ROPE>(a, B, stream) : hg == 2 ? launch_split<4, 2, ROPE>(a, B, stream)
+         : hg == 4 ? launch_split<4, 4, ROPE>(a, B, stream) : launch_split<4, 8, ROPE>(a, B, stream);
 }
 
 hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const AppendArgs& app, const void* q,
@@ -787,20 +949,12 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   a.B = L.B;
   a.rotate = rotate;
   a.scale_log2 = scale_log2;
+  a.rope_tab = L.rope ? reinterpret_cast<const float*>(base + L.rope_off) : nullptr;
+  a.rope_in = L.rope ? reinterpret_cast<const float*>(base + L.ropein_off) : nullptr;
   const int hg = L.Hq / L.Hkv;
   hipError_t e;
   if (prof_start && hipEventRecord(prof_start, stream) != hipSuccess) return hipGetLastError();
-  if (L.bits == 2) {
-    e = hg == 1 ? launch_split<2, 1>(a, L.B, stream)
-        : hg == 2 ? launch_split<2, 2>(a, L.B, stream)
-        : hg == 4 ? launch_split<2, 4>(a, L.B, stream)
-                  : launch_split<2, 8>(a, L.B, stream);
-  } else {
-    e = hg == 1 ? launch_split<4, 1>(a, L.B, stream)
-        : hg == 2 ? launch_split<4, 2>(a, L.B, stream)
-        : hg == 4 ? launch_split<4, 4>(a, L.B, stream)
-                  : launch_split<4, 8>(a, L.B, stream);
-  }
+  e = L.rope ? launch_split_for<true>(a, L.bits, hg, L.B, stream) : launch_split_for<false>(a, L.bits, hg, L.B, stream);
   if (e != hipSuccess) return e;
   if (prof_stop && hipEventRecord(prof_stop, stream) != hipSuccess) return hipGetLastError();
   return launch_combine(a.part, out, L.Hq, L.B, plan, L.win_blocks, stream);

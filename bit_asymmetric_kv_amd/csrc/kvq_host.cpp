@@ -68,6 +68,11 @@ kvq_status validate(const kvq_config* cfg) {
   if (cfg->max_tokens < 1 || cfg->max_tokens > (int64_t(1) << 30))
     return fail(KVQ_ERR_INVALID_ARG, "max_tokens must be in [1, 2^30]");
   if (cfg->sink != 0 && cfg->sink != 1) return fail(KVQ_ERR_INVALID_ARG, "sink must be 0 or 1");
+  if (cfg->rope != 0 && cfg->rope != 1) return fail(KVQ_ERR_INVALID_ARG, "rope must be 0 or 1");
+  if (cfg->rope && cfg->rotate)
+    return fail(KVQ_ERR_INVALID_ARG, "pre-RoPE keys and the Walsh-Hadamard rotation cannot be combined");
+  if (!(cfg->rope_base >= 0.0f) || std::isinf(cfg->rope_base) || (cfg->rope_base > 0.0f && cfg->rope_base <= 1.0f))
+    return fail(KVQ_ERR_INVALID_ARG, "rope_base must be 0 (10000) or a finite value above 1");
   if (!(cfg->softmax_scale >= 0.0f) || std::isinf(cfg->softmax_scale))
     return fail(KVQ_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   return ok();
@@ -83,6 +88,7 @@ Layout make_layout(const kvq_config* cfg) {
   L.W = cfg->residual + kvq::kGroup;
   L.sink = cfg->sink;
   L.RS = L.W + L.sink;
+  L.rope = cfg->rope;
   L.gcap = (cfg->max_tokens + kvq::kGroup - 1) / kvq::kGroup;
   L.group_bytes = kvq_group_bytes(cfg->bits);
   int64_t ms = (L.gcap + kvq::kMinGroupsPerSplit - 1) / kvq::kMinGroupsPerSplit;
@@ -101,6 +107,12 @@ Layout make_layout(const kvq_config* cfg) {
   off = align256(off + ring);
   L.part_off = off;
   off = align256(off + size_t(L.B) * L.Hq * size_t(L.max_splits + L.win_blocks) * kvq::kPartialStride * 4);
+  // rotary tables: one row per group start position, enough for every window chunk too
+  L.rope_entries = L.rope ? int32_t(L.gcap + 4) : 0;
+  L.rope_off = off;
+  off = align256(off + size_t(L.rope_entries) * kvq::kHeadDim * 4);
+  L.ropein_off = off;
+  off = align256(off + (L.rope ? size_t(kvq::kGroup) * kvq::kHeadDim * 4 : 0));
   L.total = off;
   return L;
 }
@@ -204,6 +216,14 @@ kvq_status kvq_create(const kvq_config* cfg, void* dev_mem, size_t dev_bytes, hi
   if (hipMemsetAsync(c->base + L.seq_off, 0, sizeof(SeqDesc) * cfg->batch, stream) != hipSuccess) {
     kvq_destroy(c);
     return fail(KVQ_ERR_HIP, "clearing sequence state failed: %s", hipGetErrorString(hipGetLastError()));
+  }
+  if (L.rope) {
+    const double rb = cfg->rope_base > 0.0f ? double(cfg->rope_base) : 10000.0;
+    const hipError_t e = kvq::launch_rope_tables(L, c->base, rb, stream);
+    if (e != hipSuccess) {
+      kvq_destroy(c);
+      return fail(KVQ_ERR_HIP, "building the rotary tables failed: %s", hipGetErrorString(e));
+    }
   }
   *out = c;
   return ok();
@@ -504,8 +524,8 @@ kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const 
     // splits in proportion to its length. With unequal lengths the splits are made
     // three times finer, so that the last splits of the sequences even out.
     if (c->resident_blocks == 0)
-      c->resident_blocks = std::max(1, kvq::decode_resident_blocks(c->cfg.bits,
-                                                                   c->cfg.num_q_heads / c->cfg.num_kv_heads));
+      c->resident_blocks = std::max(1, kvq::decode_resident_blocks(
+                                            c->cfg.bits, c->cfg.num_q_heads / c->cfg.num_kv_heads, c->cfg.rope));
     const int64_t win = int64_t(B) * Hkv * c->L.win_blocks;
     const int64_t slots = std::max<int64_t>(int64_t(B) * Hkv,
                                             c->resident_blocks - std::min<int64_t>(win, c->resident_blocks / 4));

@@ -71,11 +71,15 @@ struct Layout {
   int32_t B, Hq, Hkv, bits, R, W;  // W = R + G window slots (token t >= o in slot t % W)
   int32_t sink;                     // 1: token 0 is an attention sink, kept in ring slot W
   int32_t RS;                       // ring slots per (b, h): W + sink
+  int32_t rope;                     // 1: keys are pre-RoPE, rotated after dequantization
+  int32_t rope_entries;             // rows of the rotary table (group start positions)
   int64_t gcap;                     // group blocks per (b, h)
   size_t group_bytes;
   int32_t max_splits;
   int32_t win_blocks;  // FP16-window decode workgroups per (b, h)
-  size_t seq_off, blocks_off, ringk_off, ringv_off, part_off, total;
+  size_t seq_off, blocks_off, ringk_off, ringv_off, part_off;
+  size_t rope_off, ropein_off;  // rotary tables (pre-RoPE caches): [rope_entries][128], [32][128] fp32
+  size_t total;
 };
 
 // Launchers (return hipGetLastError() of the launch).
@@ -86,7 +90,8 @@ hipError_t launch_ring_write(const Layout& L, uint8_t* base, const SeqArgs& seq,
                              const void* v, int32_t n_max, int32_t max_ring_tokens, int rotate,
                              hipStream_t stream);
 // Workgroups of the decode split kernel that fit on the current device at once.
-int decode_resident_blocks(int bits, int hg);
+int decode_resident_blocks(int bits, int hg, int rope);
+hipError_t launch_rope_tables(const Layout& L, uint8_t* base, double rope_base, hipStream_t stream);
 hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const AppendArgs& app,
                          const void* q, float* out, int32_t groups_per_split, const SplitPlan& plan,
                          float scale_log2, int rotate, hipStream_t stream, hipEvent_t prof_start,

@@ -81,6 +81,14 @@ typedef struct {
                             good; groups then cover tokens [1 + gG, 1 + (g+1)G) ("KV cache
                             quantization: putting the bits in the cached vectors", full-text-skim
                             notes: keeping the first token in fp16 helps, most at 2 bits) */
+  int32_t rope;          /* 0 or 1: pre-RoPE keys. Appended keys are stored and quantized as given
+                            (before the rotary position embedding) and attention rotates every
+                            key at its position t (0-based index in its sequence) after
+                            dequantization ("KVQuant" review, Method and Key idea). The query passed
+                            to decode is already rotated at its own position. Rotary embedding:
+                            channels f and f + 64 (f < 64) turn by t * rope_base^(-f / 64):
+                            (a, b) -> (a cos - b sin, b cos + a sin). Not combined with rotate. */
+  float rope_base;       /* 0 => 10000; otherwise > 1 */
 } kvq_config;
 
 /* Bytes of device memory a cache with this configuration needs (host only).

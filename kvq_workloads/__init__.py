@@ -46,6 +46,7 @@ class Workload:
     ragged: tuple = field(default=())   # (lo, hi) inclusive per-sequence context range
     head_dim: int = HEAD_DIM
     sink: bool = False           # token 0 kept FP16 as an attention sink
+    rope: bool = False           # keys pre-RoPE, rotated after dequantization
 
     def context_lengths(self) -> np.ndarray:
         """Prefill length of every sequence."""
@@ -68,6 +69,9 @@ WORKLOADS = {
     "million_1m": Workload("million_1m", 1, 32, 8, 1048576, 1, 2, 32, 128, False, 8, 8.0, 0.0, 1004),
     "ragged_b64_wht": Workload("ragged_b64_wht", 64, 32, 8, 0, 32, 2, 32, 64, True, 8, 8.0, 0.0, 1005,
                                ragged=(2048, 32768)),
+    # the headline shape with pre-RoPE keys and an attention sink
+    "gqa_128k_2bit_rope": Workload("gqa_128k_2bit_rope", 1, 32, 8, 131072, 1, 2, 32, 128, False, 4, 10.0, 3.0,
+                                   1006, sink=True, rope=True),
 }
 
 

@@ -28,10 +28,11 @@ class Pair:
         self.dev = device
         self.gpu = kvq.KVCache(w.batch, w.num_q_heads, w.num_kv_heads, bits=w.bits, group=w.group,
                                residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=device,
-                               sink=w.sink)
+                               sink=w.sink, rope=w.rope)
         if groups_per_split:
             self.gpu.set_decode_split(groups_per_split)
-        self.ref = OracleCache(w.batch, w.num_q_heads, w.num_kv_heads, w.bits, w.residual, w.rotate, sink=w.sink)
+        self.ref = OracleCache(w.batch, w.num_q_heads, w.num_kv_heads, w.bits, w.residual, w.rotate, sink=w.sink,
+                               rope=w.rope)
         self.T = np.zeros(w.batch, dtype=np.int64)
         self.step = 0
 

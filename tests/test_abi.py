@@ -42,7 +42,7 @@ def _status(cfg):
     ("batch", 0), ("num_kv_heads", 0), ("num_q_heads", 12), ("head_dim", 64), ("bits", 3), ("bits", 8),
     ("group", 64), ("residual", 48), ("residual", -32), ("rotate", 2), ("max_tokens", 0),
     ("max_tokens", 1 << 31), ("softmax_scale", -1.0), ("softmax_scale", float("inf")), ("sink", 2),
-    ("sink", -1),
+    ("sink", -1), ("rope", 2), ("rope_base", 0.5), ("rope_base", float("inf")), ("rope_base", -3.0),
 ])
 def test_invalid_configs_rejected_before_any_device_call(field, value):
     cfg = kvq.make_config(2, 32, 8, residual=128, max_tokens=1000)
@@ -50,6 +50,18 @@ def test_invalid_configs_rejected_before_any_device_call(field, value):
     s, msg = _status(cfg)
     assert s == _lib.KVQ_ERR_INVALID_ARG, (field, value, s, msg)
     assert msg
+
+
+def test_rope_with_hadamard_rotation_rejected():
+    cfg = kvq.make_config(1, 8, 8, residual=32, max_tokens=100, rotate=True, rope=True)
+    assert _status(cfg)[0] == _lib.KVQ_ERR_INVALID_ARG
+
+
+def test_rope_cache_holds_its_rotary_tables():
+    plain = kvq.cache_bytes(kvq.make_config(1, 32, 8, residual=128, max_tokens=131072))
+    rope = kvq.cache_bytes(kvq.make_config(1, 32, 8, residual=128, max_tokens=131072, rope=True))
+    # one 512-byte row per group start (4096 groups) plus the 16 KB in-group table
+    assert rope - plain >= 4096 * 512 + 32 * 128 * 4
 
 
 def test_gqa_ratio_16_rejected():

@@ -37,11 +37,13 @@ def _check_blocks(cache, oh, b, h, group_sample):
         blk = got[g] if got is not None else cache.read_groups(b, h, g, 1)[0]
         exp = oh.block(g)
         assert np.array_equal(blk, exp), f"group block (b={b}, h={h}, g={g}) differs"
-    W = cache.ring_len
+    W = cache.cfg.residual + cache.cfg.group
     rk, rv = cache.read_ring(b, h, "k"), cache.read_ring(b, h, "v")
-    for t in range(oh.Q, oh.T):
-        assert np.array_equal(rk[t % W].view(np.uint16), oh.k16[t].view(np.uint16)), f"ring key t={t}"
-        assert np.array_equal(rv[t % W].view(np.uint16), oh.v16[t].view(np.uint16)), f"ring value t={t}"
+    # window tokens [o + Q, T) in slot t % W; an attention sink (token 0) in slot W
+    slots = [(t, t % W) for t in range(oh.o + oh.Q, oh.T)] + ([(0, W)] if oh.sink and oh.T else [])
+    for t, slot in slots:
+        assert np.array_equal(rk[slot].view(np.uint16), oh.k16[t].view(np.uint16)), f"ring key t={t}"
+        assert np.array_equal(rv[slot].view(np.uint16), oh.v16[t].view(np.uint16)), f"ring value t={t}"
 
 
 def _run_full(w, dev, sample, steps, check_steps, group_sample=lambda ng: range(ng)):
@@ -49,8 +51,9 @@ def _run_full(w, dev, sample, steps, check_steps, group_sample=lambda ng: range(
     lens = w.context_lengths()
     max_tokens = int(lens.max()) + steps + 1
     cache = kvq.KVCache(w.batch, w.num_q_heads, w.num_kv_heads, bits=w.bits, group=w.group,
-                        residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=dev)
-    oracles = {bh: OracleHead(w.bits, w.residual, w.rotate) for bh in sample}
+                        residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=dev,
+                        sink=w.sink, rope=w.rope)
+    oracles = {bh: OracleHead(w.bits, w.residual, w.rotate, sink=w.sink, rope=w.rope) for bh in sample}
     params = wl.torch_key_params(torch, w, dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 101 + 7)
@@ -109,6 +112,11 @@ def test_full_gqa_128k(dev, name):
 def test_full_million_1m(dev):
     sample = lambda ng: list(range(0, ng, 97)) + list(range(ng - 40, ng))
     _run_full(wl.WORKLOADS["million_1m"], dev, [(0, 3)], 1, {0}, group_sample=sample)
+
+
+def test_full_gqa_128k_rope_sink(dev):
+    # pre-RoPE keys (rotated after dequantization) with an attention sink, two steps
+    _run_full(wl.WORKLOADS["gqa_128k_2bit_rope"], dev, [(0, 1), (0, 6)], 2, {0, 1})
 
 
 def test_full_ragged_b64_wht(dev):
