@@ -18,7 +18,8 @@ What it computes, in the pages' order:
   vectors", full-text-skim notes on the fixed outlier channels of keys and the
   per-token confinement of values).
 * Asymmetric uniform quantizer: 2^b levels between the group's min and max, with
-  a scale and a zero-point ("KVQuant" review, Problem: 4 levels at 2 bits).
+  a scale and a zero-point ("KVQuant" review, Problem: 8 levels at 3 bits, 4 at
+  2 bits); b = 2, 3 or 4.
 * The most recent tokens stay in FP16 ("The Asymmetric Key-Value Cache Compression
   Framework", In practice); quantized groups are appended along the token
   dimension and combined with the FP16 residual inside attention
@@ -108,8 +109,8 @@ def quantize_uniform(x: np.ndarray, bits: int, axis: int):
     s16, z16), where s16/z16 have `axis` removed. Every step is an explicit fp32
     (or fp16 storage) rounding as stated in the module docstring.
     """
-    if bits not in (2, 4):
-        raise ValueError("bits must be 2 or 4")
+    if bits not in (2, 3, 4):
+        raise ValueError("bits must be 2, 3 or 4")
     x16 = np.asarray(x, dtype=_F16)
     x32 = x16.astype(_F32)
     levels = _F32(2 ** bits - 1)
@@ -164,7 +165,8 @@ def group_block_bytes(bits: int) -> int:
 
 
 def _code_position(o, lane, slot, bits):
-    """Byte offset of the 32-bit word and bit offset inside it for a code.
+    """Byte offset of the 32-bit word and bit offset inside it for a code (2 and
+    4 bits: one field per code).
 
     Codes of one section (keys or values) are addressed by (operand o in [0, 8),
     lane in [0, 64), slot in [0, 8)).
@@ -183,6 +185,28 @@ def _code_position(o, lane, slot, bits):
         word = 1024 * (o // 4) + 16 * lane + 4 * (o % 4)
         bit = 8 * (slot % 4) + 4 * (slot // 4)
     return word, bit
+
+
+def _code_fields(o, lane, slot, bits):
+    """Fields (word byte offset, bit offset, width, code bit) holding one code.
+
+    2 and 4 bits: one field of the code's full width (see _code_position).
+    3 bits: the two low bits in a 1024-byte plane, word at byte 16*lane + 4*(o//2),
+    bit 8*(slot % 4) + 4*(slot // 4) + 2*(o % 2); the high bit in a 512-byte plane
+    after it, word at byte 1024 + 8*lane + 4*(o // 4), bit 8*(slot % 4) +
+    4*(slot // 4) + (o % 4). (With both fields in place a lane's code nibbles line
+    up as in the 4-bit layout.)
+    """
+    if bits != 3:
+        word, bit = _code_position(o, lane, slot, bits)
+        return [(word, bit, bits, 0)]
+    o = np.asarray(o)
+    lane = np.asarray(lane)
+    slot = np.asarray(slot)
+    base_bit = 8 * (slot % 4) + 4 * (slot // 4)
+    lo = (16 * lane + 4 * (o // 2), base_bit + 2 * (o % 2), 2, 0)
+    hi = (1024 + 8 * lane + 4 * (o // 4), base_bit + (o % 4), 1, 2)
+    return [lo, hi]
 
 
 def _key_code_coords(i, d):
@@ -209,11 +233,12 @@ def _value_scale_index(i, j):
 
 
 def _section_positions(coords_fn, bits):
-    """For every code (i, d) of a section: its 32-bit word index and bit offset."""
+    """For every code (i, d) of a section, per field: 32-bit word index, bit
+    offset, width and the code bit the field starts at."""
     ii, dd = np.meshgrid(np.arange(GROUP), np.arange(HEAD_DIM), indexing="ij")
     o, lane, slot = coords_fn(ii, dd)
-    word, bit = _code_position(o, lane, slot, bits)
-    return (word // 4).astype(np.int64), bit.astype(np.uint32)
+    return [((word // 4).astype(np.int64), np.asarray(bit).astype(np.uint32), width, shift)
+            for word, bit, width, shift in _code_fields(o, lane, slot, bits)]
 
 
 _POS_CACHE = {}
@@ -227,16 +252,19 @@ def _positions(coords_fn, bits):
 
 
 def _pack_section(codes, coords_fn, bits, nbytes):
-    widx, bit = _positions(coords_fn, bits)
     words = np.zeros(nbytes // 4, dtype=np.uint32)
-    np.bitwise_or.at(words, widx.ravel(), (codes.astype(np.uint32) << bit).ravel())
+    c = codes.astype(np.uint32)
+    for widx, bit, width, shift in _positions(coords_fn, bits):
+        field = (c >> np.uint32(shift)) & np.uint32(2 ** width - 1)
+        np.bitwise_or.at(words, widx.ravel(), (field << bit).ravel())
     return words
 
 
 def _unpack_section(words, coords_fn, bits):
-    widx, bit = _positions(coords_fn, bits)
-    mask = np.uint32(2 ** bits - 1)
-    return ((words[widx] >> bit) & mask).astype(np.uint8)
+    out = np.zeros((GROUP, HEAD_DIM), dtype=np.uint32)
+    for widx, bit, width, shift in _positions(coords_fn, bits):
+        out |= ((words[widx] >> bit) & np.uint32(2 ** width - 1)) << np.uint32(shift)
+    return out.astype(np.uint8)
 
 
 def _value_scale_indices():

@@ -37,7 +37,7 @@ def test_flush_steps_of_32k_context_r128():
     assert flushes == [32800, 32832]
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("R", [0, 32, 64])
 @pytest.mark.parametrize("rotate", [False, True])
 def test_oracle_matches_bruteforce(bits, R, rotate):

@@ -14,7 +14,7 @@ import pytest
 
 from oracle import (dequantize_block, group_block_bytes, pack_group_block, quantize_key_group,
                     quantize_uniform, quantize_value_group, unpack_group_block)
-from oracle.kvq_oracle import _key_code_coords, _value_code_coords, _code_position, _value_scale_index
+from oracle.kvq_oracle import _key_code_coords, _value_code_coords, _code_position, _code_fields, _value_scale_index
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -41,7 +41,7 @@ def _rand_groups(rng, n, bits):
     return x
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_invariants_random(bits):
     rng = np.random.default_rng(10 + bits)
     x = _rand_groups(rng, 4000, bits)
@@ -118,7 +118,7 @@ def test_axes_key_per_channel_value_per_token():
     assert np.array_equal(vz, (np.arange(32)[:, None] + np.arange(4)[None, :]).astype(np.float16))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_pack_unpack_roundtrip(bits):
     rng = np.random.default_rng(7 + bits)
     L = 2 ** bits - 1
@@ -129,7 +129,7 @@ def test_pack_unpack_roundtrip(bits):
     vs = rng.standard_normal((32, 4)).astype(np.float16)
     vz = rng.standard_normal((32, 4)).astype(np.float16)
     blk = pack_group_block(kc, ks, kz, vc, vs, vz, bits)
-    assert blk.size == group_block_bytes(bits) == {2: 3072, 4: 5120}[bits]
+    assert blk.size == group_block_bytes(bits) == {2: 3072, 3: 4096, 4: 5120}[bits]
     out = unpack_group_block(blk, bits)
     for a, b in zip(out, (kc, ks, kz, vc, vs, vz)):
         assert np.array_equal(a, b)
@@ -145,6 +145,37 @@ def test_code_positions_are_a_bijection(bits, section):
     assert np.all(bit % bits == 0)
     assert len(np.unique(flat_bit)) == 32 * 128
     assert flat_bit.min() == 0 and flat_bit.max() == 32 * 128 * bits - bits
+
+
+def test_3bit_fields_are_a_bijection():
+    for fn in (_key_code_coords, _value_code_coords):
+        ii, dd = np.meshgrid(np.arange(32), np.arange(128), indexing="ij")
+        lo, hi = _code_fields(*fn(ii, dd), 3)
+        lo_bits = (lo[0] * 8 + lo[1]).ravel()
+        hi_bits = (hi[0] * 8 + hi[1]).ravel()
+        assert lo[2] == 2 and hi[2] == 1 and lo[3] == 0 and hi[3] == 2
+        assert np.all(lo[1] % 2 == 0)
+        # the low fields tile bits [0, 8192) two at a time, the high fields [8192, 12288) one at a time
+        assert len(np.unique(lo_bits)) == 4096 and lo_bits.min() == 0 and lo_bits.max() == 8190
+        assert len(np.unique(hi_bits)) == 4096 and hi_bits.min() == 8192 and hi_bits.max() == 12287
+
+
+@pytest.mark.parametrize("entry", _load("block_layout.json")["code_positions_3bit"],
+                         ids=lambda e: f'3{e["section"][0]}-{e["token"]}-{e["channel"]}')
+def test_single_3bit_code_lands_at_hand_derived_positions(entry):
+    kc = np.zeros((32, 128), dtype=np.uint8)
+    vc = np.zeros((32, 128), dtype=np.uint8)
+    target = kc if entry["section"] == "key" else vc
+    target[entry["token"], entry["channel"]] = 7   # all three bits set
+    z = np.zeros(128, dtype=np.float16)
+    zv = np.zeros((32, 4), dtype=np.float16)
+    blk = pack_group_block(kc, z, z, vc, zv, zv, 3)
+    sec = blk[:1536] if entry["section"] == "key" else blk[1536:3072]
+    words = sec.view("<u4")
+    nz = np.nonzero(words)[0].tolist()
+    assert nz == [entry["lo_word_byte"] // 4, entry["hi_word_byte"] // 4]
+    assert int(words[nz[0]]) == 3 << entry["lo_bit"]
+    assert int(words[nz[1]]) == 1 << entry["hi_bit"]
 
 
 @pytest.mark.parametrize("entry", _load("block_layout.json")["code_positions"],
