@@ -214,7 +214,44 @@ __global__ __launch_bounds__(64) void flush_wave_kernel(uint8_t* __restrict__ bl
   // operand d/16 in lane d%16 + 16((i%16)/4).
   uint32_t* kw = reinterpret_cast<uint32_t*>(blk);
   uint32_t* vw = reinterpret_cast<uint32_t*>(blk + CB);
-  constexpr int NW = CB / 4;
+  if constexpr (BITS == 3) {
+    // Bits 0-1 of the codes: word (lane l, operand pair ohi), slot s of operand
+    // 2 ohi + par at bit 8(s%4) + 4(s/4) + 2 par. Bit 2: word (lane l, operand
+    // quad oq) at byte 1024 + 8 l + 4 oq, operand 4 oq + r at bit 8(s%4) + 4(s/4) + r.
+    for (int w = lane; w < 256; w += 64) {
+      uint32_t kword = 0, vword = 0;
+      const int l = w / 4, ohi = w % 4;
+      for (int par = 0; par < 2; par++) {
+        const int o = 2 * ohi + par;
+        for (int s2 = 0; s2 < 8; s2++) {
+          const int bit = 8 * (s2 % 4) + 4 * (s2 / 4) + 2 * par;
+          const int ki = 16 * (o % 2) + l % 16, kd = 32 * (o / 2) + 8 * (l / 16) + s2;
+          const int vd = 16 * o + l % 16, vi = value_token(l / 16, s2);
+          kword |= uint32_t(ck[ki][kd] & 3) << bit;
+          vword |= uint32_t(cv[vi][vd] & 3) << bit;
+        }
+      }
+      kw[w] = kword;
+      vw[w] = vword;
+    }
+    for (int w = lane; w < 128; w += 64) {
+      uint32_t kword = 0, vword = 0;
+      const int l = w / 2, oq = w % 2;
+      for (int r2 = 0; r2 < 4; r2++) {
+        const int o = 4 * oq + r2;
+        for (int s2 = 0; s2 < 8; s2++) {
+          const int bit = 8 * (s2 % 4) + 4 * (s2 / 4) + r2;
+          const int ki = 16 * (o % 2) + l % 16, kd = 32 * (o / 2) + 8 * (l / 16) + s2;
+          const int vd = 16 * o + l % 16, vi = value_token(l / 16, s2);
+          kword |= uint32_t(ck[ki][kd] >> 2) << bit;
+          vword |= uint32_t(cv[vi][vd] >> 2) << bit;
+        }
+      }
+      kw[256 + w] = kword;
+      vw[256 + w] = vword;
+    }
+  }
+  constexpr int NW = BITS == 3 ? 0 : CB / 4;
   for (int w = lane; w < NW; w += 64) {
     uint32_t kword = 0, vword = 0;
     if (BITS == 2) {
@@ -293,6 +330,9 @@ hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqArgs& seq, cons
   auto* vin = static_cast<const __half*>(v);
   if (L.bits == 2)
     hipLaunchKernelGGL(flush_wave_kernel<2>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
+                       L.RS, L.sink, (long long)L.gcap, n_max, rotate);
+  else if (L.bits == 3)
+    hipLaunchKernelGGL(flush_wave_kernel<3>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
                        L.RS, L.sink, (long long)L.gcap, n_max, rotate);
   else
     hipLaunchKernelGGL(flush_wave_kernel<4>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,

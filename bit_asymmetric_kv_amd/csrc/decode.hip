@@ -94,6 +94,14 @@ __device__ inline half8 code_operand(const uint4& w0, const uint4& w1, int o) {
   if constexpr (BITS == 2) {
     uint32_t w = (o / 2 == 0) ? w0.x : (o / 2 == 1) ? w0.y : (o / 2 == 2) ? w0.z : w0.w;
     return codes2_to_half8((w >> (2 * (o % 2))) & 0x33333333u);
+  } else if constexpr (BITS == 3) {
+    // bits 0-1 from the 2-bit plane (w0), bit 2 from the 1-bit plane (w1.x, w1.y);
+    // both in the 4-bit nibble order, so the 4-bit conversion finishes the job
+    const uint32_t w = (o / 2 == 0) ? w0.x : (o / 2 == 1) ? w0.y : (o / 2 == 2) ? w0.z : w0.w;
+    const uint32_t hw = o < 4 ? w1.x : w1.y;
+    const uint32_t lo = (w >> (2 * (o % 2))) & 0x33333333u;
+    const uint32_t hi = (hw >> (o % 4)) & 0x11111111u;
+    return codes4_to_half8(lo | (hi << 2));
   } else {
     const uint4& v = o < 4 ? w0 : w1;
     uint32_t w = (o % 4 == 0) ? v.x : (o % 4 == 1) ? v.y : (o % 4 == 2) ? v.z : v.w;
@@ -365,7 +373,7 @@ __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt,
 // The bytes of one group block that a lane uses.
 template <int BITS, int NJ>
 struct GroupRegs {
-  uint4 kc0, kc1, vc0, vc1;  // key / value code words (kc1, vc1 used at 4 bits)
+  uint4 kc0, kc1, vc0, vc1;  // key / value code words (kc1, vc1: 4-bit second half, 3-bit high-bit plane)
   half8 ks, kz;              // key scale / zero of this lane's 8-channel block
   half8 vs[NJ], vz[NJ];      // value scale / zero of this lane's 8 tokens per channel group
 };
@@ -460,6 +468,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     if constexpr (BITS == 4) {
       G.kc1 = *reinterpret_cast<const uint4*>(blk + 1024 + 16 * lane);
       G.vc1 = *reinterpret_cast<const uint4*>(blk + CB + 1024 + 16 * lane);
+    } else if constexpr (BITS == 3) {  // the lane's 8 bytes of the 1-bit plane
+      const uint2 kh = *reinterpret_cast<const uint2*>(blk + 1024 + 8 * lane);
+      const uint2 vh = *reinterpret_cast<const uint2*>(blk + CB + 1024 + 8 * lane);
+      G.kc1 = make_uint4(kh.x, kh.y, 0u, 0u);
+      G.vc1 = make_uint4(vh.x, vh.y, 0u, 0u);
     }
     if constexpr (ROPE) {
       // lanes 0-31: the key scale / zero-point region; lanes 32-63: the rotary
@@ -908,6 +921,9 @@ int resident_blocks_for(int bits, int hg) {
   if (bits == 2)
     return hg == 1 ? resident_blocks_of<2, 1, ROPE>() : hg == 2 ? resident_blocks_of<2, 2, ROPE>()
            : hg == 4 ? resident_blocks_of<2, 4, ROPE>() : resident_blocks_of<2, 8, ROPE>();
+  if (bits == 3)
+    return hg == 1 ? resident_blocks_of<3, 1, ROPE>() : hg == 2 ? resident_blocks_of<3, 2, ROPE>()
+           : hg == 4 ? resident_blocks_of<3, 4, ROPE>() : resident_blocks_of<3, 8, ROPE>();
   return hg == 1 ? resident_blocks_of<4, 1, ROPE>() : hg == 2 ? resident_blocks_of<4, 2, ROPE>()
          : hg == 4 ? resident_blocks_of<4, 4, ROPE>() : resident_blocks_of<4, 8, ROPE>();
 }
@@ -921,6 +937,9 @@ hipError_t launch_split_for(const DecodeArgs& a, int bits, int hg, int B, hipStr
   if (bits == 2)
     return hg == 1 ? launch_split<2, 1, ROPE>(a, B, stream) : hg == 2 ? launch_split<2, 2, ROPE>(a, B, stream)
            : hg == 4 ? launch_split<2, 4, ROPE>(a, B, stream) : launch_split<2, 8, ROPE>(a, B, stream);
+  if (bits == 3)
+    return hg == 1 ? launch_split<3, 1, ROPE>(a, B, stream) : hg == 2 ? launch_split<3, 2, ROPE>(a, B, stream)
+           : hg == 4 ? launch_split<3, 4, ROPE>(a, B, stream) : launch_split<3, 8, ROPE>(a, B, stream);
   return hg == 1 ? launch_split<4, 1, ROPE>(a, B, stream) : hg == 2 ? launch_split<4, 2, ROPE>(a, B, stream)
          : hg == 4 ? launch_split<4, 4, ROPE>(a, B, stream) : launch_split<4, 8, ROPE>(a, B, stream);
 }

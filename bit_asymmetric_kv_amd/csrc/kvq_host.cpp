@@ -55,8 +55,8 @@ kvq_status validate(const kvq_config* cfg) {
     return fail(KVQ_ERR_INVALID_ARG, "num_q_heads / num_kv_heads must be 1, 2, 4 or 8 (got %d)", ratio);
   if (cfg->head_dim != kvq::kHeadDim)
     return fail(KVQ_ERR_INVALID_ARG, "head_dim must be 128 (got %d)", cfg->head_dim);
-  if (cfg->bits != 2 && cfg->bits != 4)
-    return fail(KVQ_ERR_INVALID_ARG, "bits must be 2 or 4 (got %d)", cfg->bits);
+  if (cfg->bits < 2 || cfg->bits > 4)
+    return fail(KVQ_ERR_INVALID_ARG, "bits must be 2, 3 or 4 (got %d)", cfg->bits);
   if (cfg->group != kvq::kGroup)
     return fail(KVQ_ERR_INVALID_ARG, "group must be 32 (got %d)", cfg->group);
   if (cfg->head_dim % cfg->group)
@@ -140,7 +140,7 @@ struct kvq_cache {
 extern "C" {
 
 size_t kvq_group_bytes(int32_t bits) {
-  if (bits != 2 && bits != 4) return 0;
+  if (bits < 2 || bits > 4) return 0;
   return size_t(2) * kvq::kGroup * kvq::kHeadDim * bits / 8 + 512 + 512;
 }
 

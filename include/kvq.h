@@ -8,9 +8,9 @@
  *    ("The Asymmetric Key-Value Cache Compression Framework", Summary and
  *    Method; "KV cache quantization: putting the bits in the cached vectors",
  *    full-text-skim notes on KIVI);
- *  - codes use a fixed number of bits per element, 2 or 4 ("Read What Matters",
- *    the NOVA-KV abstract on a fixed per-token bit count; "KVQuant" review,
- *    Problem and Results on 2..4-bit widths);
+ *  - codes use a fixed number of bits per element, 2, 3 or 4 ("Read What
+ *    Matters", the NOVA-KV abstract on a fixed per-token bit count; "KVQuant"
+ *    review, Problem: 8 levels at 3 bits, 4 at 2 bits);
  *  - the most recent R tokens stay FP16 ("The Asymmetric Key-Value Cache
  *    Compression Framework", In practice), and quantized groups are appended along
  *    the token dimension and combined with that FP16 residual inside attention
@@ -71,7 +71,7 @@ typedef struct {
   int32_t num_q_heads;   /* Hq; a multiple of num_kv_heads */
   int32_t num_kv_heads;  /* Hkv >= 1; Hq / Hkv must be 1, 2, 4 or 8 */
   int32_t head_dim;      /* D; must be 128 */
-  int32_t bits;          /* 2 or 4 */
+  int32_t bits;          /* 2, 3 or 4 */
   int32_t group;         /* G: tokens per key group = channels per value group; must be 32 */
   int32_t residual;      /* R >= 0 and a multiple of G: FP16 window of the most recent tokens */
   int32_t rotate;        /* 0 or 1: normalized Walsh-Hadamard transform on q and k */
@@ -159,7 +159,8 @@ enum {
   KVQ_PART_RING_V = 2  /* FP16 value window of (b, h), same layout */
 };
 
-/* Bytes of one packed 32-token group block: 3072 at 2 bits, 5120 at 4 bits.
+/* Bytes of one packed 32-token group block: 3072 at 2 bits, 4096 at 3 bits, 5120 at 4
+ * bits (0 for other widths).
  * Block layout (little-endian): [key codes | value codes | key scale fp16[128] |
  * key zero fp16[128] | value scales fp16[128] | value zeros fp16[128]].
  * Code words: a code is addressed by (operand o in 0..7, lane l in 0..63,
@@ -167,7 +168,10 @@ enum {
  * l = i%16 + 16*((d%32)/8), s = d%8. Value token i, channel d: o = d/16,
  * l = d%16 + 16*((i%16)/4), s = 4*(i/16) + i%4.
  *   2-bit: 32-bit word at byte 16*l + 4*(o/2), bits from 8*(s/2) + 4*(s%2) + 2*(o%2);
- *   4-bit: 32-bit word at byte 1024*(o/4) + 16*l + 4*(o%4), bits from 8*(s%4) + 4*(s/4).
+ *   4-bit: 32-bit word at byte 1024*(o/4) + 16*l + 4*(o%4), bits from 8*(s%4) + 4*(s/4);
+ *   3-bit: code bits 0-1 in the 32-bit word at byte 16*l + 4*(o/2), bits from
+ *          8*(s%4) + 4*(s/4) + 2*(o%2); code bit 2 in the word at byte
+ *          1024 + 8*l + 4*(o/4), bit 8*(s%4) + 4*(s/4) + o%4.
  * Value scale and zero of token i, channel group j sit at fp16 index
  * (4*((i%16)/4) + j)*8 + 4*(i/16) + i%4 of their 128-entry arrays. */
 size_t kvq_group_bytes(int32_t bits);

@@ -65,6 +65,7 @@ WORKLOADS = {
     "tiny_mha_4k": Workload("tiny_mha_4k", 1, 8, 8, 4096, 1, 2, 32, 32, False, 4, 10.0, 0.0, 1001),
     "llama2_7b_b8_32k": Workload("llama2_7b_b8_32k", 8, 32, 32, 32768, 64, 2, 32, 128, False, 8, 8.0, 0.0, 1002),
     "gqa_128k_2bit": Workload("gqa_128k_2bit", 1, 32, 8, 131072, 1, 2, 32, 128, False, 4, 10.0, 3.0, 1003),
+    "gqa_128k_3bit": Workload("gqa_128k_3bit", 1, 32, 8, 131072, 1, 3, 32, 128, False, 4, 10.0, 3.0, 1003),
     "gqa_128k_4bit": Workload("gqa_128k_4bit", 1, 32, 8, 131072, 1, 4, 32, 128, False, 4, 10.0, 3.0, 1003),
     "million_1m": Workload("million_1m", 1, 32, 8, 1048576, 1, 2, 32, 128, False, 8, 8.0, 0.0, 1004),
     "ragged_b64_wht": Workload("ragged_b64_wht", 64, 32, 8, 0, 32, 2, 32, 64, True, 8, 8.0, 0.0, 1005,

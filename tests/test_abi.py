@@ -28,7 +28,8 @@ def test_library_exports_every_declared_function():
 def test_group_bytes():
     assert kvq.group_bytes(2) == 3072
     assert kvq.group_bytes(4) == 5120
-    assert kvq.group_bytes(3) == 0
+    assert kvq.group_bytes(3) == 4096
+    assert kvq.group_bytes(5) == 0
 
 
 def _status(cfg):
@@ -39,7 +40,7 @@ def _status(cfg):
 
 
 @pytest.mark.parametrize("field,value", [
-    ("batch", 0), ("num_kv_heads", 0), ("num_q_heads", 12), ("head_dim", 64), ("bits", 3), ("bits", 8),
+    ("batch", 0), ("num_kv_heads", 0), ("num_q_heads", 12), ("head_dim", 64), ("bits", 1), ("bits", 5), ("bits", 8),
     ("group", 64), ("residual", 48), ("residual", -32), ("rotate", 2), ("max_tokens", 0),
     ("max_tokens", 1 << 31), ("softmax_scale", -1.0), ("softmax_scale", float("inf")), ("sink", 2),
     ("sink", -1), ("rope", 2), ("rope_base", 0.5), ("rope_base", float("inf")), ("rope_base", -3.0),

@@ -104,7 +104,7 @@ def test_full_llama2_7b_b8_32k(dev):
     _run_full(wl.WORKLOADS["llama2_7b_b8_32k"], dev, [(0, 0), (3, 17), (7, 31)], 64, {0, 31, 32, 63})
 
 
-@pytest.mark.parametrize("name", ["gqa_128k_2bit", "gqa_128k_4bit"])
+@pytest.mark.parametrize("name", ["gqa_128k_2bit", "gqa_128k_3bit", "gqa_128k_4bit"])
 def test_full_gqa_128k(dev, name):
     _run_full(wl.WORKLOADS[name], dev, [(0, 0), (0, 5)], 1, {0})
 

@@ -42,7 +42,7 @@ def test_tiny_mha_full_size(dev):
     _run(w, [w.context], w.steps, dev)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_llama_shape_reduced(dev, bits):
     w = wl.WORKLOADS["llama2_7b_b8_32k"].scaled(batch=2, bits=bits)
     _run(w, [1000, 1000], 40, dev, check_every=8)
@@ -74,7 +74,7 @@ def test_batch_above_inline_records(dev):
 
 
 @pytest.mark.parametrize("ratio", [1, 2, 4, 8])
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_gqa_ratios(dev, ratio, bits):
     w = wl.WORKLOADS["gqa_128k_2bit"].scaled(num_q_heads=2 * ratio, num_kv_heads=2, bits=bits, residual=32,
                                               name=f"ratio{ratio}")
@@ -85,6 +85,12 @@ def test_gqa_ratios(dev, ratio, bits):
 @pytest.mark.parametrize("T", [1, 31, 32, 33, 63, 64, 65, 95, 96, 97])
 def test_edge_lengths(dev, R, T):
     w = wl.WORKLOADS["gqa_128k_2bit"].scaled(batch=1, residual=R, name=f"edge_R{R}")
+    _run(w, [T], 2, dev)
+
+
+@pytest.mark.parametrize("T", [1, 32, 33, 64, 65, 97])
+def test_edge_lengths_3bit(dev, T):
+    w = wl.WORKLOADS["gqa_128k_2bit"].scaled(batch=1, residual=0, bits=3, name="edge3")
     _run(w, [T], 2, dev)
 
 
@@ -150,7 +156,7 @@ def _adversarial_groups():
     return k, v
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_adversarial_groups_bit_exact(dev, bits):
     import bit_asymmetric_kv_amd as kvq
     from oracle import OracleHead

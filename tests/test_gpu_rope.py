@@ -42,7 +42,7 @@ def test_rope_edge_lengths(dev, R, T):
     _two_call(w, [T], 2, dev)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("ratio", [1, 2, 4, 8])
 def test_rope_gqa_ratios(dev, bits, ratio):
     w = wl.WORKLOADS["gqa_128k_2bit"].scaled(num_q_heads=2 * ratio, num_kv_heads=2, bits=bits, residual=32,

@@ -41,7 +41,7 @@ def test_sink_edge_lengths(dev, R, T):
     _two_call(w, [T], 2, dev)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_sink_llama_shape(dev, bits):
     w = wl.WORKLOADS["llama2_7b_b8_32k"].scaled(batch=2, bits=bits, sink=True, name="sink_llama")
     _two_call(w, [1000, 1001], 40, dev, check_every=8)

@@ -58,7 +58,7 @@ def test_step_single_token_crossing_flushes(dev):
     _run(w, [100], lambda s: [1], 70, dev, check_every=7)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_step_ragged_multi_token_and_empty(dev, bits):
     w = wl.WORKLOADS["llama2_7b_b8_32k"].scaled(batch=5, num_q_heads=8, num_kv_heads=4, residual=64, bits=bits,
                                                    name="step_ragged")
