@@ -31,6 +31,7 @@ EXPORTED = (
     "kvq_cache_bytes", "kvq_create", "kvq_append", "kvq_decode_attention", "kvq_set_decode_split",
     "kvq_destroy", "kvq_seq_len", "kvq_group_bytes", "kvq_read_state", "kvq_last_error",
     "kvq_set_profile_events", "kvq_decode_step", "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention",
+    "kvq_set_pages", "kvq_reset_sequence",
 )
 
 
@@ -49,6 +50,8 @@ class KVQConfig(ctypes.Structure):
         ("sink", ctypes.c_int32),
         ("rope", ctypes.c_int32),
         ("rope_base", ctypes.c_float),
+        ("page_groups", ctypes.c_int32),
+        ("pool_pages", ctypes.c_int64),
     ]
 
 
@@ -101,9 +104,12 @@ def load() -> ctypes.CDLL:
     lib.kvq_stream_read.argtypes = [vp, sz, vp, vp]
     lib.kvq_fp16_workspace_bytes.argtypes = [f16p, ctypes.POINTER(sz)]
     lib.kvq_fp16_decode_attention.argtypes = [f16p, vp, vp, vp, i64, vp, vp, vp, sz, vp]
+    lib.kvq_set_pages.argtypes = [vp, i32, ctypes.POINTER(i32), i32, vp]
+    lib.kvq_reset_sequence.argtypes = [vp, i32]
     for name in ("kvq_cache_bytes", "kvq_create", "kvq_append", "kvq_decode_attention",
                  "kvq_set_decode_split", "kvq_seq_len", "kvq_read_state", "kvq_set_profile_events",
-                 "kvq_decode_step", "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention"):
+                 "kvq_decode_step", "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention",
+                 "kvq_set_pages", "kvq_reset_sequence"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -116,11 +122,11 @@ def check(status: int) -> None:
 
 def make_config(batch, num_q_heads, num_kv_heads, head_dim=128, bits=2, group=32, residual=128,
                 rotate=False, max_tokens=4096, softmax_scale=0.0, sink=False, rope=False,
-                rope_base=0.0) -> KVQConfig:
+                rope_base=0.0, page_groups=0, pool_pages=0) -> KVQConfig:
     def flag(x):
         return int(bool(x)) if x in (True, False) else int(x)
     return KVQConfig(batch, num_q_heads, num_kv_heads, head_dim, bits, group, residual, flag(rotate),
-                     max_tokens, softmax_scale, flag(sink), flag(rope), rope_base)
+                     max_tokens, softmax_scale, flag(sink), flag(rope), rope_base, page_groups, pool_pages)
 
 
 def cache_bytes(cfg: KVQConfig) -> int:
@@ -142,11 +148,11 @@ class KVCache:
 
     def __init__(self, batch, num_q_heads, num_kv_heads, head_dim=128, bits=2, group=32, residual=128,
                  rotate=False, max_tokens=4096, softmax_scale=0.0, device="cuda", sink=False, rope=False,
-                 rope_base=0.0):
+                 rope_base=0.0, page_groups=0, pool_pages=0):
         import torch
         self._torch = torch
         self.cfg = make_config(batch, num_q_heads, num_kv_heads, head_dim, bits, group, residual,
-                               rotate, max_tokens, softmax_scale, sink, rope, rope_base)
+                               rotate, max_tokens, softmax_scale, sink, rope, rope_base, page_groups, pool_pages)
         self.device = torch.device(device)
         nbytes = cache_bytes(self.cfg)
         self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -235,6 +241,16 @@ class KVCache:
 
     def set_decode_split(self, groups_per_split: int):
         check(load().kvq_set_decode_split(self._handle, int(groups_per_split)))
+
+    def set_pages(self, b: int, pages):
+        """Paged caches: the pool pages of sequence b, in group order."""
+        arr = (ctypes.c_int32 * max(1, len(pages)))(*[int(p) for p in pages])
+        check(load().kvq_set_pages(self._handle, int(b), arr, len(pages),
+                                   ctypes.c_void_p(_stream_ptr(self._torch, self.device))))
+
+    def reset_sequence(self, b: int):
+        """Start sequence b over (a paged cache frees its pages)."""
+        check(load().kvq_reset_sequence(self._handle, int(b)))
 
     def set_profile_events(self, start_event: int, stop_event: int):
         """Raw hipEvent_t handles recorded around the decode split kernel (0, 0 to stop)."""

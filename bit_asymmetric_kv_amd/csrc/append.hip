@@ -108,12 +108,11 @@ __device__ inline QuantOut quantize_regs(const float* x, uint8_t* codes) {
 }
 
 template <int BITS>
-__global__ __launch_bounds__(64) void flush_wave_kernel(uint8_t* __restrict__ blocks,
-                                                        const __half* __restrict__ ringk,
+__global__ __launch_bounds__(64) void flush_wave_kernel(const GroupStore store, const __half* __restrict__ ringk,
                                                         const __half* __restrict__ ringv, const SeqArgs seq,
                                                         const __half* __restrict__ kin,
                                                         const __half* __restrict__ vin, int Hkv, int W, int RS,
-                                                        int sink, long long gcap, int n_max, int rotate) {
+                                                        int sink, int n_max, int rotate) {
   constexpr int CB = kG * kD * BITS / 8;  // bytes of one code section
   constexpr int GB = 2 * CB + 1024;
   __shared__ uint8_t ck[kG][kD];  // key codes [token][channel]
@@ -132,7 +131,7 @@ __global__ __launch_bounds__(64) void flush_wave_kernel(uint8_t* __restrict__ bl
     return t < sd.t_old ? ring + (bh * RS + size_t(t % W)) * kD
                         : in + ((size_t(b) * n_max + (t - sd.t_old)) * Hkv + h) * kD;
   };
-  uint8_t* blk = blocks + (bh * size_t(gcap) + g) * GB;
+  uint8_t* blk = store.at(b, h, g);
 
   // Every load of the group is issued before any arithmetic: 32 key words (channels
   // 2l, 2l+1 of each token) and the lane's two 64-byte value segments.
@@ -323,20 +322,20 @@ __global__ __launch_bounds__(128) void ring_write_kernel(__half* __restrict__ ri
 hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqArgs& seq, const void* k, const void* v,
                         int32_t n_max, int32_t max_flush_groups, int rotate, hipStream_t stream) {
   dim3 grid(max_flush_groups, L.Hkv, L.B);
-  auto* blocks = base + L.blocks_off;
+  const GroupStore blocks = group_store(L, base);
   auto* rk = reinterpret_cast<const __half*>(base + L.ringk_off);
   auto* rv = reinterpret_cast<const __half*>(base + L.ringv_off);
   auto* kin = static_cast<const __half*>(k);
   auto* vin = static_cast<const __half*>(v);
   if (L.bits == 2)
     hipLaunchKernelGGL(flush_wave_kernel<2>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
-                       L.RS, L.sink, (long long)L.gcap, n_max, rotate);
+                       L.RS, L.sink, n_max, rotate);
   else if (L.bits == 3)
     hipLaunchKernelGGL(flush_wave_kernel<3>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
-                       L.RS, L.sink, (long long)L.gcap, n_max, rotate);
+                       L.RS, L.sink, n_max, rotate);
   else
     hipLaunchKernelGGL(flush_wave_kernel<4>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
-                       L.RS, L.sink, (long long)L.gcap, n_max, rotate);
+                       L.RS, L.sink, n_max, rotate);
   return hipGetLastError();
 }
 

@@ -40,13 +40,12 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 struct DecodeArgs {
-  const uint8_t* blocks;
+  GroupStore store;  // packed group blocks (contiguous or paged)
   __half* ringk;  // written only by a folded append, for its new window tokens
   __half* ringv;
   const SeqDesc* seq;
   const __half* q;
   float* part;
-  long long gcap;
   int B, Hkv, Hq, W, gps, rotate;
   int RS, sink;  // ring slots per (sequence, kv-head): W, plus slot W for an attention sink
   int wblocks;   // FP16-window workgroups per (sequence, kv-head)
@@ -389,7 +388,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int U = 2 * HG;
   constexpr int NCOPY = 16 / HG;                // columns per head
   constexpr int NJ = NCOPY >= 4 ? 1 : 4 / NCOPY;  // value channel groups handled per lane
-  constexpr int GB = 2 * (kG * kD * BITS / 8) + 1024;
   constexpr int ITEMS = (HG + 3) / 4;         // key-side operand items per lane
 
   __shared__ float wpart_mem[kWaves * HG * kPartialStride];  // per-wave partials
@@ -458,10 +456,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // Wave-uniform (the wave index is), so the loop's waits branch on scalars.
   const int n = __builtin_amdgcn_readfirstlane(tail ? 0 : max(0, wg1 - wg0));
 
-  const uint8_t* base = a.blocks + (size_t(b) * a.Hkv + h) * size_t(a.gcap) * GB;
   // Group r's bytes of this lane, loaded straight into registers.
   auto load_group = [&](int r, GroupRegs<BITS, NJ>& G) {
-    const uint8_t* blk = base + size_t(wg0 + r) * GB;
+    const uint8_t* blk = a.store.at(b, h, wg0 + r);
     constexpr int CB = kG * kD * BITS / 8;
     G.kc0 = *reinterpret_cast<const uint4*>(blk + 16 * lane);
     G.vc0 = *reinterpret_cast<const uint4*>(blk + CB + 16 * lane);
@@ -949,13 +946,12 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
                          hipStream_t stream,
                          hipEvent_t prof_start, hipEvent_t prof_stop) {
   DecodeArgs a;
-  a.blocks = base + L.blocks_off;
+  a.store = group_store(L, base);
   a.ringk = reinterpret_cast<__half*>(base + L.ringk_off);
   a.ringv = reinterpret_cast<__half*>(base + L.ringv_off);
   a.seq = seq;
   a.q = static_cast<const __half*>(q);
   a.part = reinterpret_cast<float*>(base + L.part_off);
-  a.gcap = L.gcap;
   a.Hkv = L.Hkv;
   a.Hq = L.Hq;
   a.W = L.W;

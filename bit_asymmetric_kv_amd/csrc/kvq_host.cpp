@@ -75,6 +75,10 @@ kvq_status validate(const kvq_config* cfg) {
     return fail(KVQ_ERR_INVALID_ARG, "rope_base must be 0 (10000) or a finite value above 1");
   if (!(cfg->softmax_scale >= 0.0f) || std::isinf(cfg->softmax_scale))
     return fail(KVQ_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (cfg->page_groups < 0 || cfg->page_groups > kvq::kMaxPageGroups)
+    return fail(KVQ_ERR_INVALID_ARG, "page_groups must be in [0, %d]", kvq::kMaxPageGroups);
+  if (cfg->page_groups > 0 && (cfg->pool_pages < 1 || cfg->pool_pages > INT32_MAX))
+    return fail(KVQ_ERR_INVALID_ARG, "pool_pages must be in [1, 2^31 - 1] for a paged cache");
   return ok();
 }
 
@@ -95,11 +99,19 @@ Layout make_layout(const kvq_config* cfg) {
   L.max_splits = int32_t(std::max<int64_t>(1, std::min<int64_t>(ms, kvq::kMaxSplits)));
   const int32_t win_chunks = L.R / kvq::kGroup + 1 + L.sink;  // window < R + G tokens, plus the sink
   L.win_blocks = (win_chunks + kvq::kWindowChunksPerBlock - 1) / kvq::kWindowChunksPerBlock;
+  L.P = cfg->page_groups;
+  L.max_pages = L.P ? int32_t((L.gcap + L.P - 1) / L.P) : 0;
+  L.pool_pages = L.P ? cfg->pool_pages : 0;
   size_t off = 0;
   L.seq_off = off;
   off = align256(off + sizeof(SeqDesc) * size_t(L.B));
+  L.table_off = off;
+  off = align256(off + sizeof(int32_t) * size_t(L.B) * size_t(L.max_pages));
   L.blocks_off = off;
-  off = align256(off + size_t(L.B) * L.Hkv * size_t(L.gcap) * L.group_bytes);
+  if (L.P)  // the page pool: [pool_pages][Hkv][P][GB]
+    off = align256(off + size_t(L.pool_pages) * L.Hkv * size_t(L.P) * L.group_bytes);
+  else
+    off = align256(off + size_t(L.B) * L.Hkv * size_t(L.gcap) * L.group_bytes);
   size_t ring = size_t(L.B) * L.Hkv * L.RS * kvq::kHeadDim * 2;
   L.ringk_off = off;
   off = align256(off + ring);
@@ -135,6 +147,12 @@ struct kvq_cache {
   SeqDesc* staging[kStaging] = {};
   hipEvent_t staging_done[kStaging] = {};
   int next_staging = 0;
+  // Paged caches: the page table (pinned host copy of the device table), the pages
+  // each sequence has, the owner of every pool page (-1: free), and the event of the
+  // last table upload (the pinned copy is not rewritten before it has passed).
+  int32_t* table = nullptr;
+  std::vector<int32_t> npages, owner;
+  hipEvent_t table_done = nullptr;
 };
 
 extern "C" {
@@ -165,6 +183,11 @@ void kvq_destroy(kvq_cache* c) {
     }
     if (c->staging[i]) hipHostFree(c->staging[i]);
   }
+  if (c->table_done) {
+    hipEventSynchronize(c->table_done);
+    hipEventDestroy(c->table_done);
+  }
+  if (c->table) hipHostFree(c->table);
   if (c->owned && c->base) hipFree(c->base);
   delete c;
 }
@@ -216,6 +239,23 @@ kvq_status kvq_create(const kvq_config* cfg, void* dev_mem, size_t dev_bytes, hi
   if (hipMemsetAsync(c->base + L.seq_off, 0, sizeof(SeqDesc) * cfg->batch, stream) != hipSuccess) {
     kvq_destroy(c);
     return fail(KVQ_ERR_HIP, "clearing sequence state failed: %s", hipGetErrorString(hipGetLastError()));
+  }
+  if (L.P) {
+    const size_t tb = sizeof(int32_t) * size_t(L.B) * size_t(L.max_pages);
+    if (hipHostMalloc(reinterpret_cast<void**>(&c->table), tb) != hipSuccess ||
+        hipEventCreateWithFlags(&c->table_done, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      kvq_destroy(c);
+      return fail(KVQ_ERR_HIP, "pinned page-table allocation failed");
+    }
+    std::fill(c->table, c->table + size_t(L.B) * L.max_pages, 0);
+    c->npages.assign(cfg->batch, 0);
+    c->owner.assign(size_t(L.pool_pages), -1);
+    // unassigned entries point at page 0, which always exists
+    if (hipMemsetAsync(c->base + L.table_off, 0, tb, stream) != hipSuccess) {
+      kvq_destroy(c);
+      return fail(KVQ_ERR_HIP, "clearing the page table failed: %s", hipGetErrorString(hipGetLastError()));
+    }
   }
   if (L.rope) {
     const double rb = cfg->rope_base > 0.0f ? double(cfg->rope_base) : 10000.0;
@@ -283,6 +323,13 @@ kvq_status prepare_append(kvq_cache* c, const void* k, const void* v, const int3
     if (c->T[b] + n > c->cfg.max_tokens)
       return fail(KVQ_ERR_CAPACITY, "sequence %d would hold %lld tokens > max_tokens %lld", b,
                   (long long)(c->T[b] + n), (long long)c->cfg.max_tokens);
+    if (c->L.P) {
+      const int64_t groups = quantized_count(c->T[b] + n, c->cfg.residual, c->cfg.sink) / kvq::kGroup;
+      const int64_t need = (groups + c->L.P - 1) / c->L.P;
+      if (need > c->npages[b])
+        return fail(KVQ_ERR_CAPACITY, "sequence %d needs %lld pages for its groups and has %d", b,
+                    (long long)need, c->npages[b]);
+    }
     pa.total_new += n;
   }
   pa.T2 = c->T;
@@ -419,9 +466,86 @@ kvq_status kvq_read_state(kvq_cache* c, int32_t part, int32_t b, int32_t h, size
     return fail(KVQ_ERR_INVALID_ARG, "range [%zu, %zu) exceeds the part's %zu bytes", offset,
                 offset + bytes, region);
   if (bytes == 0) return ok();
+  if (part == KVQ_PART_GROUPS && L.P) {
+    // paged: gather page by page through the table
+    const size_t gb = L.group_bytes;
+    const kvq::GroupStore st = kvq::group_store(L, c->base);
+    size_t done = 0;
+    while (done < bytes) {
+      const size_t pos = offset + done;
+      const int64_t g = int64_t(pos / gb);
+      if (g / L.P >= c->npages[b])
+        return fail(KVQ_ERR_INVALID_ARG, "group %lld of sequence %d has no page", (long long)g, b);
+      const size_t run = std::min(bytes - done, size_t(L.P - g % L.P) * gb - pos % gb);
+      const size_t src = st.offset(b, h, g, c->table[size_t(b) * L.max_pages + g / L.P]) + pos % gb;
+      if (hipMemcpyAsync(static_cast<uint8_t*>(host_dst) + done, c->base + L.blocks_off + src, run,
+                         hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return fail(KVQ_ERR_HIP, "reading state failed: %s", hipGetErrorString(hipGetLastError()));
+      done += run;
+    }
+    if (hipStreamSynchronize(stream) != hipSuccess)
+      return fail(KVQ_ERR_HIP, "reading state failed: %s", hipGetErrorString(hipGetLastError()));
+    return ok();
+  }
   if (hipMemcpyAsync(host_dst, c->base + start + offset, bytes, hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
     return fail(KVQ_ERR_HIP, "reading state failed: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+kvq_status kvq_set_pages(kvq_cache* c, int32_t b, const int32_t* pages, int32_t n, hipStream_t stream) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  const Layout& L = c->L;
+  if (!L.P) return fail(KVQ_ERR_INVALID_ARG, "the cache is not paged (page_groups == 0)");
+  if (b < 0 || b >= c->cfg.batch) return fail(KVQ_ERR_INVALID_ARG, "sequence index %d out of range", b);
+  if (n < 0 || n > L.max_pages)
+    return fail(KVQ_ERR_INVALID_ARG, "n = %d outside [0, %d] pages per sequence", n, L.max_pages);
+  if (n && !pages) return fail(KVQ_ERR_INVALID_ARG, "pages is NULL");
+  int32_t* row = c->table + size_t(b) * L.max_pages;
+  // pages holding quantized groups keep their place
+  const int64_t used = (c->Q[b] / kvq::kGroup + L.P - 1) / L.P;
+  if (n < used) return fail(KVQ_ERR_INVALID_ARG, "sequence %d holds groups in %lld pages; n = %d", b,
+                            (long long)used, n);
+  std::vector<int32_t> seen;
+  seen.reserve(n);
+  for (int32_t i = 0; i < n; i++) {
+    const int32_t p = pages[i];
+    if (p < 0 || int64_t(p) >= L.pool_pages)
+      return fail(KVQ_ERR_INVALID_ARG, "page %d outside the pool of %lld", p, (long long)L.pool_pages);
+    if (c->owner[p] != -1 && c->owner[p] != b)
+      return fail(KVQ_ERR_INVALID_ARG, "page %d belongs to sequence %d", p, c->owner[p]);
+    if (i < used && p != row[i])
+      return fail(KVQ_ERR_INVALID_ARG, "page %d of sequence %d holds groups and cannot move", i, b);
+    seen.push_back(p);
+  }
+  std::sort(seen.begin(), seen.end());
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
+    return fail(KVQ_ERR_INVALID_ARG, "a page appears twice");
+  if (hipEventSynchronize(c->table_done) != hipSuccess)
+    return fail(KVQ_ERR_HIP, "waiting for the previous table upload failed");
+  for (int32_t i = 0; i < c->npages[b]; i++) c->owner[row[i]] = -1;
+  for (int32_t i = 0; i < n; i++) {
+    row[i] = pages[i];
+    c->owner[pages[i]] = b;
+  }
+  c->npages[b] = n;
+  if (n && (hipMemcpyAsync(c->base + L.table_off + sizeof(int32_t) * size_t(b) * L.max_pages, row,
+                           sizeof(int32_t) * size_t(n), hipMemcpyHostToDevice, stream) != hipSuccess ||
+            hipEventRecord(c->table_done, stream) != hipSuccess))
+    return fail(KVQ_ERR_HIP, "uploading the page table failed: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+kvq_status kvq_reset_sequence(kvq_cache* c, int32_t b) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  if (b < 0 || b >= c->cfg.batch) return fail(KVQ_ERR_INVALID_ARG, "sequence index %d out of range", b);
+  c->T[b] = 0;
+  c->Q[b] = 0;
+  if (c->L.P) {
+    const int32_t* row = c->table + size_t(b) * c->L.max_pages;
+    for (int32_t i = 0; i < c->npages[b]; i++) c->owner[row[i]] = -1;
+    c->npages[b] = 0;
+  }
   return ok();
 }
 

@@ -12,6 +12,7 @@ constexpr int kPartialStride = kHeadDim + 2;  // m (log2 domain), l, o[128] per 
 constexpr int kMinGroupsPerSplit = 4;
 constexpr int kMaxSplits = 2048;
 constexpr int kMaxResidual = 4096;
+constexpr int kMaxPageGroups = 1 << 16;  // groups per page of a paged cache
 // The FP16 window [o + Q, T) holds at most residual + group - 1 tokens: residual / 32
 // + 1 chunks of 32 tokens, plus one chunk for an attention sink; four chunks per
 // decode workgroup.
@@ -67,22 +68,57 @@ struct SplitPlan {
   int32_t pstride;
 };
 
+// Where the packed group blocks live. Contiguous caches: [B][Hkv][gcap][GB].
+// Paged caches: a pool of pages, each [Hkv][P][GB] for P consecutive groups of one
+// sequence; table[b][g / P] names the page of group g of sequence b.
+struct GroupStore {
+  uint8_t* blocks;
+  const int32_t* table;  // [B][max_pages]; null for a contiguous cache
+  long long gcap;
+  int Hkv, P, max_pages, gb;
+  __host__ __device__ size_t offset(int b, int h, long long g, int page) const {
+    if (!table) return ((size_t(b) * Hkv + h) * size_t(gcap) + size_t(g)) * size_t(gb);
+    return ((size_t(page) * Hkv + h) * size_t(P) + size_t(g % P)) * size_t(gb);
+  }
+  // Device side: looks the page up in the table.
+  __device__ uint8_t* at(int b, int h, long long g) const {
+    const int page = table ? __builtin_amdgcn_readfirstlane(table[size_t(b) * max_pages + g / P]) : 0;
+    return blocks + offset(b, h, g, page);
+  }
+};
+
 struct Layout {
   int32_t B, Hq, Hkv, bits, R, W;  // W = R + G window slots (token t >= o in slot t % W)
   int32_t sink;                     // 1: token 0 is an attention sink, kept in ring slot W
   int32_t RS;                       // ring slots per (b, h): W + sink
   int32_t rope;                     // 1: keys are pre-RoPE, rotated after dequantization
   int32_t rope_entries;             // rows of the rotary table (group start positions)
+  int32_t P;                        // paged caches: groups per page (0: contiguous)
+  int32_t max_pages;                // paged caches: table entries per sequence
+  int64_t pool_pages;               // paged caches: pages in the pool
   int64_t gcap;                     // group blocks per (b, h)
   size_t group_bytes;
   int32_t max_splits;
   int32_t win_blocks;  // FP16-window decode workgroups per (b, h)
-  size_t seq_off, blocks_off, ringk_off, ringv_off, part_off;
+  size_t seq_off, table_off, blocks_off, ringk_off, ringv_off, part_off;
   size_t rope_off, ropein_off;  // rotary tables (pre-RoPE caches): [rope_entries][128], [32][128] fp32
   size_t total;
 };
 
 // Launchers (return hipGetLastError() of the launch).
+// The group store of a cache laid out by L at base.
+inline GroupStore group_store(const Layout& L, uint8_t* base) {
+  GroupStore s;
+  s.blocks = base + L.blocks_off;
+  s.table = L.P ? reinterpret_cast<const int32_t*>(base + L.table_off) : nullptr;
+  s.gcap = L.gcap;
+  s.Hkv = L.Hkv;
+  s.P = L.P > 0 ? L.P : 1;
+  s.max_pages = L.max_pages;
+  s.gb = int(L.group_bytes);
+  return s;
+}
+
 hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqArgs& seq, const void* k,
                         const void* v, int32_t n_max, int32_t max_flush_groups, int rotate,
                         hipStream_t stream);

@@ -89,6 +89,13 @@ typedef struct {
                             channels f and f + 64 (f < 64) turn by t * rope_base^(-f / 64):
                             (a, b) -> (a cos - b sin, b cos + a sin). Not combined with rotate. */
   float rope_base;       /* 0 => 10000; otherwise > 1 */
+  int32_t page_groups;   /* 0: each (sequence, kv-head) owns room for max_tokens tokens of groups.
+                            P > 0: paged cache (the "KVQuant" review's Limitations and "Where this
+                            paper sits" name paged serving stacks as where such caches must fit;
+                            its "Sparks" list suggests blocked or paged allocation): a pool of pool_pages pages, each holding P consecutive
+                            groups of one sequence for all its kv-heads, laid out [Hkv][P][group
+                            block]; the caller assigns pages with kvq_set_pages. P <= 65536. */
+  int64_t pool_pages;    /* pages in the pool of a paged cache (1 .. 2^31 - 1); ignored otherwise */
 } kvq_config;
 
 /* Bytes of device memory a cache with this configuration needs (host only).
@@ -147,13 +154,28 @@ kvq_status kvq_set_profile_events(kvq_cache* c, hipEvent_t start, hipEvent_t sto
  * frees library-allocated memory. */
 void kvq_destroy(kvq_cache* c);
 
+/* Paged caches: give sequence b the pool pages pages[0..n), page i holding its groups
+ * [i*P, (i+1)*P). Pages that already hold quantized groups of b (the first
+ * ceil(Q/(32 P)) entries) must stay where they are; every page id must be in
+ * [0, pool_pages), appear once, and not belong to another sequence. Pages of b that
+ * are dropped become free. An append whose groups would need more pages than b has
+ * fails with KVQ_ERR_CAPACITY and changes nothing. The table update is ordered on
+ * `stream`; the caller keeps no ownership of `pages` after the call.
+ * Errors: KVQ_ERR_INVALID_ARG (cache not paged, bad index, range, ownership). */
+kvq_status kvq_set_pages(kvq_cache* c, int32_t b, const int32_t* pages, int32_t n, hipStream_t stream);
+
+/* Start sequence b over (T = Q = 0); in a paged cache its pages become free.
+ * Host-side only: the next append rewrites what the kernels read. */
+kvq_status kvq_reset_sequence(kvq_cache* c, int32_t b);
+
 /* Host mirror of sequence b: T = tokens appended, Q = tokens held quantized
  * (tokens [o, o + Q), o = 1 with an attention sink, else 0). */
 kvq_status kvq_seq_len(const kvq_cache* c, int32_t b, int64_t* T, int64_t* Q);
 
 /* Parts of the state that kvq_read_state can copy out. */
 enum {
-  KVQ_PART_GROUPS = 0, /* packed group blocks of (b, h): group g at byte g * kvq_group_bytes() */
+  KVQ_PART_GROUPS = 0, /* packed group blocks of (b, h): group g at byte g * kvq_group_bytes()
+                          (gathered through the page table in a paged cache) */
   KVQ_PART_RING_K = 1, /* FP16 key window of (b, h): [R + G + sink][D], token t in slot
                           t % (R + G), except an attention sink (token 0) in slot R + G */
   KVQ_PART_RING_V = 2  /* FP16 value window of (b, h), same layout */

@@ -21,14 +21,14 @@ def to_dev(x, torch, dev):
 class Pair:
     """A GPU cache and its oracle twin fed with identical inputs."""
 
-    def __init__(self, w: wl.Workload, max_tokens: int, device, torch, groups_per_split=0):
+    def __init__(self, w: wl.Workload, max_tokens: int, device, torch, groups_per_split=0, **cache_kw):
         import bit_asymmetric_kv_amd as kvq
         self.w = w
         self.torch = torch
         self.dev = device
         self.gpu = kvq.KVCache(w.batch, w.num_q_heads, w.num_kv_heads, bits=w.bits, group=w.group,
                                residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=device,
-                               sink=w.sink, rope=w.rope)
+                               sink=w.sink, rope=w.rope, **cache_kw)
         if groups_per_split:
             self.gpu.set_decode_split(groups_per_split)
         self.ref = OracleCache(w.batch, w.num_q_heads, w.num_kv_heads, w.bits, w.residual, w.rotate, sink=w.sink,
