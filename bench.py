@@ -76,19 +76,28 @@ class HipEvents:
 PREFILL_CHUNK = 131072
 
 
-def build_caches(torch, kvq, w, copies, max_tokens, dev, gps, ev=None, stream=None):
+def build_caches(torch, kvq, w, copies, max_tokens, dev, gps, ev=None, stream=None, page_groups=0):
     """Build `copies` caches holding the workload's prefill (appends of up to
     PREFILL_CHUNK tokens per sequence: one append for contexts up to 128K).
     With `ev`, each copy's appends are timed (inputs drawn beforehand) and the
-    per-copy prefill times in ms are returned as well."""
+    per-copy prefill times in ms are returned as well. With `page_groups`, each cache
+    is paged and every sequence gets its pages in a seeded random order."""
     params = wl.torch_key_params(torch, w, dev)
     caches, times = [], []
     lens = w.context_lengths()
     chunk = PREFILL_CHUNK
     for c in range(copies):
+        paged = {}
+        if page_groups:
+            max_pages = -(-((max_tokens + w.group - 1) // w.group) // page_groups)
+            paged = dict(page_groups=page_groups, pool_pages=w.batch * max_pages)
         cache = kvq.KVCache(w.batch, w.num_q_heads, w.num_kv_heads, bits=w.bits, group=w.group,
                             residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=dev,
-                            sink=w.sink, rope=w.rope)
+                            sink=w.sink, rope=w.rope, **paged)
+        if page_groups:
+            perm = np.random.default_rng(w.seed + c).permutation(w.batch * max_pages)
+            for b in range(w.batch):
+                cache.set_pages(b, perm[b * max_pages:(b + 1) * max_pages].tolist())
         if gps:
             cache.set_decode_split(gps)
         gen = torch.Generator(device=dev)
@@ -282,6 +291,8 @@ def main():
     ap.add_argument("--workload", default="gqa_128k_2bit", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--copies", type=int, default=8, help="independent caches stepped round-robin")
     ap.add_argument("--groups-per-split", type=int, default=0)
+    ap.add_argument("--page-groups", type=int, default=0,
+                    help="paged caches with this many groups per page (pages in random order)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparisons", action="store_true",
                     help="skip the streaming-read probe and the FP16-cache decode")
@@ -307,7 +318,7 @@ def main():
     ev = HipEvents()
     stream = torch.cuda.current_stream(dev).cuda_stream
     caches, params, prefill_ms = build_caches(torch, kvq, w, args.copies, max_tokens, dev, args.groups_per_split,
-                                              ev, stream)
+                                              ev, stream, args.page_groups)
     # Prefill-side quantization throughput: every copy's prefill appends, timed.
     lens = w.context_lengths()
     pf_tokens = int(lens.sum())
@@ -443,7 +454,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "context": int(w.context_lengths().max()), "bits": w.bits,
-                   "group": w.group, "residual": w.residual, "rotate": w.rotate,
+                   "group": w.group, "residual": w.residual, "rotate": w.rotate, "sink": w.sink,
+                   "pre_rope": w.rope, "page_groups": args.page_groups,
                    "caches_round_robin": args.copies, "parallelism": "single GPU"},
         "step": {"algorithmic_bytes": int(bytes_avg), "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
                  "two_call_us_per_step": round(two_call_us, 2),

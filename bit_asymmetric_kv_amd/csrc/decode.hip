@@ -451,7 +451,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int g1 = min(ng, g0 + a.gps);
   const int len = tail ? 0 : max(0, g1 - g0);
   const int per = (len + kWaves - 1) / kWaves;
-  const int wg0 = g0 + wave * per;
+  // wave-uniform (kept in scalar registers: a paged cache's table entries are then
+  // scalar loads)
+  const int wg0 = __builtin_amdgcn_readfirstlane(g0 + wave * per);
   const int wg1 = min(g1, wg0 + per);
   // Wave-uniform (the wave index is), so the loop's waits branch on scalars.
   const int n = __builtin_amdgcn_readfirstlane(tail ? 0 : max(0, wg1 - wg0));

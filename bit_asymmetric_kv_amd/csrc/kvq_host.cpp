@@ -75,8 +75,9 @@ kvq_status validate(const kvq_config* cfg) {
     return fail(KVQ_ERR_INVALID_ARG, "rope_base must be 0 (10000) or a finite value above 1");
   if (!(cfg->softmax_scale >= 0.0f) || std::isinf(cfg->softmax_scale))
     return fail(KVQ_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-  if (cfg->page_groups < 0 || cfg->page_groups > kvq::kMaxPageGroups)
-    return fail(KVQ_ERR_INVALID_ARG, "page_groups must be in [0, %d]", kvq::kMaxPageGroups);
+  if (cfg->page_groups < 0 || cfg->page_groups > kvq::kMaxPageGroups ||
+      (cfg->page_groups & (cfg->page_groups - 1)))
+    return fail(KVQ_ERR_INVALID_ARG, "page_groups must be 0 or a power of two up to %d", kvq::kMaxPageGroups);
   if (cfg->page_groups > 0 && (cfg->pool_pages < 1 || cfg->pool_pages > INT32_MAX))
     return fail(KVQ_ERR_INVALID_ARG, "pool_pages must be in [1, 2^31 - 1] for a paged cache");
   return ok();

@@ -75,14 +75,15 @@ struct GroupStore {
   uint8_t* blocks;
   const int32_t* table;  // [B][max_pages]; null for a contiguous cache
   long long gcap;
-  int Hkv, P, max_pages, gb;
+  int Hkv, P, pshift, max_pages, gb;  // P = 2^pshift groups per page
   __host__ __device__ size_t offset(int b, int h, long long g, int page) const {
     if (!table) return ((size_t(b) * Hkv + h) * size_t(gcap) + size_t(g)) * size_t(gb);
-    return ((size_t(page) * Hkv + h) * size_t(P) + size_t(g % P)) * size_t(gb);
+    return ((size_t(page) * Hkv + h) * size_t(P) + size_t(g & (P - 1))) * size_t(gb);
   }
   // Device side: looks the page up in the table.
   __device__ uint8_t* at(int b, int h, long long g) const {
-    const int page = table ? __builtin_amdgcn_readfirstlane(table[size_t(b) * max_pages + g / P]) : 0;
+    const int page =
+        table ? __builtin_amdgcn_readfirstlane(table[size_t(b) * max_pages + size_t(g >> pshift)]) : 0;
     return blocks + offset(b, h, g, page);
   }
 };
@@ -114,6 +115,8 @@ inline GroupStore group_store(const Layout& L, uint8_t* base) {
   s.gcap = L.gcap;
   s.Hkv = L.Hkv;
   s.P = L.P > 0 ? L.P : 1;
+  s.pshift = 0;
+  while ((1 << s.pshift) < s.P) s.pshift++;
   s.max_pages = L.max_pages;
   s.gb = int(L.group_bytes);
   return s;

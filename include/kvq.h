@@ -94,7 +94,8 @@ typedef struct {
                             paper sits" name paged serving stacks as where such caches must fit;
                             its "Sparks" list suggests blocked or paged allocation): a pool of pool_pages pages, each holding P consecutive
                             groups of one sequence for all its kv-heads, laid out [Hkv][P][group
-                            block]; the caller assigns pages with kvq_set_pages. P <= 65536. */
+                            block]; the caller assigns pages with kvq_set_pages. P is a power of two
+                            up to 65536. */
   int64_t pool_pages;    /* pages in the pool of a paged cache (1 .. 2^31 - 1); ignored otherwise */
 } kvq_config;
 

@@ -44,6 +44,7 @@ def _status(cfg):
     ("group", 64), ("residual", 48), ("residual", -32), ("rotate", 2), ("max_tokens", 0),
     ("max_tokens", 1 << 31), ("softmax_scale", -1.0), ("softmax_scale", float("inf")), ("sink", 2),
     ("sink", -1), ("rope", 2), ("rope_base", 0.5), ("rope_base", float("inf")), ("rope_base", -3.0),
+    ("page_groups", 3), ("page_groups", -1), ("page_groups", 1 << 17),
 ])
 def test_invalid_configs_rejected_before_any_device_call(field, value):
     cfg = kvq.make_config(2, 32, 8, residual=128, max_tokens=1000)
@@ -51,6 +52,19 @@ def test_invalid_configs_rejected_before_any_device_call(field, value):
     s, msg = _status(cfg)
     assert s == _lib.KVQ_ERR_INVALID_ARG, (field, value, s, msg)
     assert msg
+
+
+def test_paged_cache_needs_a_pool():
+    cfg = kvq.make_config(1, 8, 8, residual=32, max_tokens=100, page_groups=4, pool_pages=0)
+    assert _status(cfg)[0] == _lib.KVQ_ERR_INVALID_ARG
+
+
+def test_paged_cache_bytes_follow_the_pool():
+    small = kvq.cache_bytes(kvq.make_config(2, 32, 8, residual=128, max_tokens=131072, page_groups=16,
+                                            pool_pages=10))
+    big = kvq.cache_bytes(kvq.make_config(2, 32, 8, residual=128, max_tokens=131072, page_groups=16,
+                                          pool_pages=110))
+    assert big - small == 100 * 8 * 16 * 3072
 
 
 def test_rope_with_hadamard_rotation_rejected():

@@ -50,7 +50,7 @@ def test_paged_random_pages_parity(dev):
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_paged_matches_contiguous_bitwise(dev, bits):
     w = _w(bits=bits, batch=2)
-    P, max_tokens = 3, 1500
+    P, max_tokens = 2, 1500
     max_pages = -(-((max_tokens + 31) // 32) // P)
     a = Pair(w, max_tokens, dev, torch, page_groups=P, pool_pages=2 * max_pages)
     b = Pair(w, max_tokens, dev, torch)
@@ -158,6 +158,8 @@ def test_paged_validation(dev):
     plain = kvq.KVCache(1, 4, 1, bits=2, residual=32, max_tokens=500, device=dev)
     with pytest.raises(kvq.KVQError):
         plain.set_pages(0, [0])                       # not a paged cache
+    with pytest.raises(kvq.KVQError):                 # page_groups must be a power of two
+        kvq.KVCache(1, 4, 1, bits=2, residual=32, max_tokens=500, device=dev, page_groups=3, pool_pages=4)
     c = kvq.KVCache(2, 4, 1, bits=2, residual=32, max_tokens=500, device=dev, page_groups=2, pool_pages=10)
     for bad in ([10], [-1], [1, 1], list(range(9))):  # range, range, duplicate, more than max_pages (8)
         with pytest.raises(kvq.KVQError) as e:
