@@ -304,7 +304,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels are per-GPU and "
-              f"this build has no multi-GPU path.", file=sys.stderr)
+              f"the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
