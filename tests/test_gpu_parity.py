@@ -191,3 +191,28 @@ def test_errors_leave_state_unchanged(dev):
     with pytest.raises(kvq.KVQError):
         cache.append(k, k, n_tokens=[61, 0])
     assert cache.seq_len(0) == (60, 0)
+
+
+@pytest.mark.parametrize("scale", [0.3, 0.02])
+def test_explicit_softmax_scale(dev, scale):
+    import bit_asymmetric_kv_amd as kvq
+    from oracle import OracleCache
+    w = wl.WORKLOADS["gqa_128k_2bit"].scaled(batch=2, num_q_heads=8, num_kv_heads=2, residual=32, name="scale")
+    print(f"case softmax_scale {scale}", flush=True)
+    cache = kvq.KVCache(w.batch, w.num_q_heads, w.num_kv_heads, bits=w.bits, residual=w.residual,
+                        max_tokens=1200, softmax_scale=scale, device=dev)
+    ref = OracleCache(w.batch, w.num_q_heads, w.num_kv_heads, w.bits, w.residual, softmax_scale=scale)
+    k, v = wl.kv_batch(w, [0, 0], 1100, np.array([1100, 700]))
+    cache.append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), n_tokens=[1100, 700])
+    ref.append(k, v, [1100, 700])
+    q = wl.queries(w, 0)
+    out = cache.decode(torch.from_numpy(q).to(dev)).cpu().numpy().astype(np.float64)
+    err = float(np.abs(out - ref.decode(q)).max())
+    assert err <= 2e-3, f"max |gpu - oracle| = {err:.3e}"
+
+
+@pytest.mark.parametrize("R,T", [(1024, 1055), (1024, 1057), (1024, 3000), (4096, 4127), (4096, 6000)])
+def test_large_residual_window(dev, R, T):
+    # windows of R .. R + 31 tokens spread over many FP16-window workgroups
+    w = wl.WORKLOADS["gqa_128k_2bit"].scaled(batch=1, residual=R, name=f"bigR{R}")
+    _run(w, [T], 2, dev)
