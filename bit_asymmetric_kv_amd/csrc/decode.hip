@@ -382,9 +382,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // MFMA columns. Key side: U = 2 * HG column kinds, the fp16 high part of head u at
   // u < HG and the low part of head U - 1 - u at u >= HG (u = column % U), repeated
   // over the 16 columns; the two parts of a score are added across the paired
-  // columns. Value side: every column keeps its head and takes one of the channel
-  // groups j; the fp16 high and low parts of its B operand go through two MFMAs into
-  // the same accumulator.
+  // columns. Value side: the same column kinds; each lane computes the high and low
+  // parts of p * s_value for its head and one channel group j (j from the column's
+  // copy), and the MFMA of a 16-channel block reads, through shared memory, the B
+  // operand of that block's channel group. The high and low columns accumulate apart
+  // and are added across the pair once, at the end.
   constexpr int U = 2 * HG;
   constexpr int NCOPY = 16 / HG;                // columns per head
   constexpr int NJ = NCOPY >= 4 ? 1 : 4 / NCOPY;  // value channel groups handled per lane
@@ -400,6 +402,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       half8 b[4][4][U];
     } bk[kWaves];
   } sh;
+  // value-side B operands per wave: [k-block][channel group j][column kind, rotated
+  // by 2 j]; kind 2 hd + part holds the high (part 0) or low (part 1) half of
+  // p * s_value of head hd
+  __shared__ half8 vstage[kWaves][4][4][U];
   // Pre-RoPE keys: in-group rotary cos / sin [32][128], and per wave the current
   // group's key scales / zero-points (512 B) and base-angle cos / sin (512 B).
   __shared__ float ropein[ROPE ? kG * kD : 1];
@@ -693,7 +699,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  auto value_side = [&](const GroupRegs<BITS, NJ>& g, const float4v& r0, const float4v& r1) {
+  // Value side, first half: online softmax of the group's scores, B = p * s_value as
+  // fp16 high and low parts to shared memory, sum p * z_value.
+  auto value_prep = [&](const GroupRegs<BITS, NJ>& g, const float4v& r0, const float4v& r1) {
     const float sc[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
     // Online softmax. Scores stay in the prescaled units S (log2 units are ex * S);
     // the running max m_run is kept in the same units.
@@ -714,20 +722,37 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], ex, negm));
       l_run += p[i];
     }
-    // Value side: B = p * s_value (fp16 high + low parts), plus sum p * z_value.
+    // B = p * s_value (fp16 high + low parts) of this lane's head and channel
+    // groups, plus sum p * z_value.
     const half8 ph = to_half8(p);
-    half8 bvh[NJ], bvl[NJ];
     for (int jr = 0; jr < NJ; jr++) {
-      split_products(p, ph, g.vs[jr], bvh[jr], bvl[jr]);
+      half8 bvh, bvl;
+      split_products(p, ph, g.vs[jr], bvh, bvl);
+      const int j = jbase + jr;
+      vstage[wave][kb][j][(2 * hd + 2 * j) % U] = bvh;
+      vstage[wave][kb][j][(2 * hd + 1 + 2 * j) % U] = bvl;
       float z = zacc[jr];
       for (int s = 0; s < 8; s++) z = __builtin_fmaf(p[s], float(g.vz[jr][s]), z);
       zacc[jr] = z;
     }
+  };
+  // Value side, second half: one MFMA per 16-channel block t against the B operand of
+  // its channel group t / 2; high- and low-part columns accumulate apart and are
+  // added across the paired columns at the end.
+  auto value_mfma = [&](const GroupRegs<BITS, NJ>& g) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int kind = 2 * hd + (ishi ? 0 : 1);
     for (int t = 0; t < 8; t++) {
-      const half8 av = code_operand<BITS>(g.vc0, g.vc1, t);
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bvh[(t / 2) % NJ], oacc[t], 0, 0, 0);
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bvl[(t / 2) % NJ], oacc[t], 0, 0, 0);
+      const int j = t / 2;
+      const half8 bv = vstage[wave][kb][j][(kind + 2 * j) % U];
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(g.vc0, g.vc1, t), bv, oacc[t], 0, 0, 0);
     }
+  };
+  auto value_side = [&](const GroupRegs<BITS, NJ>& g, const float4v& r0, const float4v& r1) {
+    value_prep(g, r0, r1);
+    value_mfma(g);
   };
 
   // Four register sets R0..R3 take the roles (group r, r+1, r+2, r+3) in turn, so nothing
@@ -739,12 +764,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
                    GroupRegs<BITS, NJ>& Gr3) {
     load_group(min(r + 3, n - 1), Gr3);
     if constexpr (ROPE) {
-      value_side(Gr, s0, s1);
+      value_prep(Gr, s0, s1);
       key_rope(Gr1, s0, s1);
+      value_mfma(Gr);
     } else {
       const float qzn = key_prep(Gr1);
-      value_side(Gr, s0, s1);
+      value_prep(Gr, s0, s1);
       key_mfma(Gr1, qzn, s0, s1);
+      value_mfma(Gr);
     }
   };
   if constexpr (ROPE) {
@@ -794,8 +821,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     wp.at(wave, hd, 1) = l_tot;
   }
   for (int t = 0; t < 8; t++) {
+    float o[4];
+    for (int i = 0; i < 4; i++) o[i] = oacc[t][i] + partner<U>(oacc[t][i]);  // high + low columns
     if (kcopy == (t / 2) / NJ)
-      for (int i = 0; i < 4; i++) wp.at(wave, hd, 2 + 16 * t + 4 * kb + i) = oacc[t][i] + zs[(t / 2) % NJ];
+      for (int i = 0; i < 4; i++) wp.at(wave, hd, 2 + 16 * t + 4 * kb + i) = o[i] + zs[(t / 2) % NJ];
   }
   merge_and_store<HG>(a, b, h, split, wp);
 }
