@@ -138,6 +138,27 @@ __device__ inline float row_max_stride4(float x) {
   return x;
 }
 
+// Max / sum over the lanes of a 16-lane row with equal lane % (16 / NR) (DPP row
+// rotations by 2, 4 and 8).
+template <int CTRL>
+__device__ inline float row_rot(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int NR>
+__device__ inline float row_class_max(float x) {
+  if constexpr (NR >= 8) x = fmaxf(x, row_rot<0x122>(x));
+  if constexpr (NR >= 4) x = fmaxf(x, row_rot<0x124>(x));
+  if constexpr (NR >= 2) x = fmaxf(x, row_rot<0x128>(x));
+  return x;
+}
+template <int NR>
+__device__ inline float row_class_sum(float x) {
+  if constexpr (NR >= 8) x += row_rot<0x122>(x);
+  if constexpr (NR >= 4) x += row_rot<0x124>(x);
+  if constexpr (NR >= 2) x += row_rot<0x128>(x);
+  return x;
+}
+
 // Sum over the four quads of a 16-lane row for lanes with equal lane % 4
 // (DPP row rotations by 4 and 8).
 __device__ inline float row_sum_stride4(float x) {
@@ -391,6 +412,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int NCOPY = 16 / HG;                // columns per head
   constexpr int NJ = NCOPY >= 4 ? 1 : 4 / NCOPY;  // value channel groups handled per lane
   constexpr int ITEMS = (HG + 3) / 4;         // key-side operand items per lane
+  constexpr int NR = 16 / U;                  // column blocks of U (copies of a column kind)
+  constexpr int SP = 8 / NR;                  // score slots whose softmax weight a lane computes
 
   __shared__ float wpart_mem[kWaves * HG * kPartialStride];  // per-wave partials
   __shared__ float qf[HG][kD];
@@ -406,6 +429,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // by 2 j]; kind 2 hd + part holds the high (part 0) or low (part 1) half of
   // p * s_value of head hd
   __shared__ half8 vstage[kWaves][4][4][U];
+  // softmax weights per wave: [k-block][head][8 slots]; the NR copies of a column
+  // kind each compute SP of the 8 and read the rest from here
+  __shared__ float pstage[NR > 1 ? kWaves : 1][4][HG][8];
   // Pre-RoPE keys: in-group rotary cos / sin [32][128], and per wave the current
   // group's key scales / zero-points (512 B) and base-angle cos / sin (512 B).
   __shared__ float ropein[ROPE ? kG * kD : 1];
@@ -542,6 +568,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const bool ishi = u < HG;
   const int hd = ishi ? u : U - 1 - u;                  // query head of this column
   const int kcopy = 2 * (col / U) + (ishi ? 0 : 1);     // which copy of the head (0..NCOPY-1)
+  const int role = col / U;                             // block of U columns (0..NR-1)
   const int jbase = (kcopy % (4 / NJ)) * NJ;            // first value channel group of the column
   // Key-side operand preparation: channel block cb = lane / 4 (8 channels) and head
   // (lane % 4) % HG + 4 * it. With this mapping the q . z_key sum of a head ends up
@@ -620,8 +647,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     else qzc = hd >= 4 ? qz[1] : qz[0];
     return ishi ? qzc : 0.0f;  // q . z_key enters once, through the high-part column
   };
-  // Key side, second half: scores of the group's 32 tokens (rows 4*kb + i of token
-  // tiles 0 and 1); the high and low parts are added across the paired columns.
+  // Key side, second half: the high- or low-part sums of the scores of the group's
+  // 32 tokens (rows 4*kb + i of token tiles 0 and 1), by column kind.
   auto key_mfma = [&](const GroupRegs<BITS, NJ>& g, float qzc, float4v& r0, float4v& r1) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -632,10 +659,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       const half8 bk = sh.bk[wave].b[kc][kb][(u + (U / 2) * kb) % U];
       r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(g.kc0, g.kc1, 2 * kc), bk, r0, 0, 0, 0);
       r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(g.kc0, g.kc1, 2 * kc + 1), bk, r1, 0, 0, 0);
-    }
-    for (int i = 0; i < 4; i++) {
-      r0[i] += partner<U>(r0[i]);
-      r1[i] += partner<U>(r1[i]);
     }
   };
 
@@ -693,23 +716,29 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         else r1 = r;
       }
     }
-    for (int i = 0; i < 4; i++) {
-      r0[i] += partner<U>(r0[i]);
-      r1[i] += partner<U>(r1[i]);
-    }
   };
 
   // Value side, first half: online softmax of the group's scores, B = p * s_value as
   // fp16 high and low parts to shared memory, sum p * z_value.
   auto value_prep = [&](const GroupRegs<BITS, NJ>& g, const float4v& r0, const float4v& r1) {
-    const float sc[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    // This lane's score slots SP * role + i (slot k: row k % 4 of tile k / 4), the
+    // high and low parts added across the paired columns (the pair shares the role).
+    float x[SP];
+    for (int i = 0; i < SP; i++) {
+      float v = i < 4 ? r0[i] : r1[i - 4];
+      for (int rr = 1; rr < NR; rr++) {
+        const int k = SP * rr + i;
+        v = role == rr ? (k < 4 ? r0[k] : r1[k - 4]) : v;
+      }
+      x[i] = v + partner<U>(v);
+    }
     // Online softmax. Scores stay in the prescaled units S (log2 units are ex * S);
     // the running max m_run is kept in the same units.
     // The cross-lane max is only formed when some score exceeds the running max.
-    float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    float mloc = x[0];
+    for (int i = 1; i < SP; i++) mloc = fmaxf(mloc, x[i]);
     if (__ballot(mloc > m_run)) {
-      const float m_new = fmaxf(m_run, wave_max_rows(mloc));
+      const float m_new = fmaxf(m_run, row_class_max<NR>(wave_max_rows(mloc)));
       const float alpha = m_run == -INFINITY ? 0.0f : exp2f(ex * (m_run - m_new));
       for (int t = 0; t < 8; t++) oacc[t] *= alpha;
       l_run *= alpha;
@@ -718,9 +747,28 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
     const float negm = -ex * m_run;
     float p[8];
-    for (int i = 0; i < 8; i++) {
-      p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], ex, negm));
-      l_run += p[i];
+    if constexpr (NR == 1) {
+      for (int i = 0; i < 8; i++) {
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], ex, negm));
+        l_run += p[i];
+      }
+    } else {
+      // each copy computes SP weights; all 8 come back through shared memory
+      float pl[SP];
+      for (int i = 0; i < SP; i++) {
+        pl[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], ex, negm));
+        l_run += pl[i];
+      }
+      float* ps = &pstage[wave][kb][hd][0];
+      if constexpr (SP == 4) *reinterpret_cast<float4*>(ps + 4 * role) = make_float4(pl[0], pl[1], pl[2], pl[3]);
+      else if constexpr (SP == 2) *reinterpret_cast<float2*>(ps + 2 * role) = make_float2(pl[0], pl[1]);
+      else ps[role] = pl[0];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const float4 pa = *reinterpret_cast<const float4*>(ps), pb = *reinterpret_cast<const float4*>(ps + 4);
+      p[0] = pa.x; p[1] = pa.y; p[2] = pa.z; p[3] = pa.w;
+      p[4] = pb.x; p[5] = pb.y; p[6] = pb.z; p[7] = pb.w;
     }
     // B = p * s_value (fp16 high + low parts) of this lane's head and channel
     // groups, plus sum p * z_value.
@@ -813,7 +861,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 
   // Wave partial: sums over the four row blocks.
-  const float l_tot = wave_sum_rows(l_run);
+  const float l_tot = row_class_sum<NR>(wave_sum_rows(l_run));
   float zs[NJ];
   for (int jr = 0; jr < NJ; jr++) zs[jr] = wave_sum_rows(zacc[jr]);
   if (kb == 0 && kcopy == 0) {
