@@ -609,8 +609,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const float exp_ = partner<U>(exh);
     ex = ishi ? exh : exp_;
   }
-  half8 qh16[ITEMS];  // fp16 copies of qreg for the high parts of the key-side operand
-  for (int it = 0; it < ITEMS; it++) qh16[it] = to_half8(qreg[it]);
+  // q = qh16 + ql16 to about 22 bits (fp16 high part and fp16 residual)
+  half8 qh16[ITEMS], ql16[ITEMS];
+  for (int it = 0; it < ITEMS; it++) {
+    qh16[it] = to_half8(qreg[it]);
+    for (int e = 0; e < 8; e++) ql16[it][e] = _Float16(qreg[it][e] - float(qh16[it][e]));
+  }
 
   float4v oacc[8];
   for (int t = 0; t < 8; t++) oacc[t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -632,7 +636,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int it = 0; it < ITEMS; it++) {
       const int hh = hh0 + 4 * it;
       half8 hi, lo;
-      split_products(qreg[it], qh16[it], g.ks, hi, lo);
+      // hi = fp16(qh * s); qh * s - hi is exact in fp16 (the rounding error of a
+      // product), so one fused fp16 operation forms it and a second adds ql * s
+      hi = qh16[it] * g.ks;
+      lo = __builtin_elementwise_fma(qh16[it], g.ks, -hi);
+      lo = __builtin_elementwise_fma(ql16[it], g.ks, lo);
       float z = 0.0f;
       for (int s = 0; s < 8; s++) z = __builtin_fmaf(qreg[it][s], float(g.kz[s]), z);
       qz[it] = wave_sum_rows(row_sum_stride4(z));
