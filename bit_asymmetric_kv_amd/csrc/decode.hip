@@ -426,8 +426,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     } bk[kWaves];
   } sh;
   // value-side B operands per wave: [k-block][channel group j][column kind, rotated
-  // by 2 j]; kind 2 hd + part holds the high (part 0) or low (part 1) half of
-  // p * s_value of head hd
+  // by j so that the eight lanes of a write hit eight different 16-byte bank groups];
+  // kind 2 hd + part holds the high (part 0) or low (part 1) half of p * s_value of
+  // head hd
   __shared__ half8 vstage[kWaves][4][4][U];
   // softmax weights per wave: [k-block][head][8 slots]; the NR copies of a column
   // kind each compute SP of the 8 and read the rest from here
@@ -768,9 +769,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         l_run += pl[i];
       }
       float* ps = &pstage[wave][kb][hd][0];
-      if constexpr (SP == 4) *reinterpret_cast<float4*>(ps + 4 * role) = make_float4(pl[0], pl[1], pl[2], pl[3]);
-      else if constexpr (SP == 2) *reinterpret_cast<float2*>(ps + 2 * role) = make_float2(pl[0], pl[1]);
-      else ps[role] = pl[0];
+      if (ishi) {  // the low-part column of the pair holds the same weights
+        if constexpr (SP == 4) *reinterpret_cast<float4*>(ps + 4 * role) = make_float4(pl[0], pl[1], pl[2], pl[3]);
+        else if constexpr (SP == 2) *reinterpret_cast<float2*>(ps + 2 * role) = make_float2(pl[0], pl[1]);
+        else ps[role] = pl[0];
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -785,8 +788,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       half8 bvh, bvl;
       split_products(p, ph, g.vs[jr], bvh, bvl);
       const int j = jbase + jr;
-      vstage[wave][kb][j][(2 * hd + 2 * j) % U] = bvh;
-      vstage[wave][kb][j][(2 * hd + 1 + 2 * j) % U] = bvl;
+      vstage[wave][kb][j][(2 * hd + j) % U] = bvh;
+      vstage[wave][kb][j][(2 * hd + 1 + j) % U] = bvl;
       float z = zacc[jr];
       for (int s = 0; s < 8; s++) z = __builtin_fmaf(p[s], float(g.vz[jr][s]), z);
       zacc[jr] = z;
@@ -802,7 +805,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const int kind = 2 * hd + (ishi ? 0 : 1);
     for (int t = 0; t < 8; t++) {
       const int j = t / 2;
-      const half8 bv = vstage[wave][kb][j][(kind + 2 * j) % U];
+      const half8 bv = vstage[wave][kb][j][(kind + j) % U];
       oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(code_operand<BITS>(g.vc0, g.vc1, t), bv, oacc[t], 0, 0, 0);
     }
   };
