@@ -168,24 +168,46 @@ __device__ inline float row_sum_stride4(float x) {
 }
 
 // (hi, lo) fp16 operand pair of the products x_i = a[i] * s[i], i = 0..7, with
-// hi + lo = x to about 21 bits: hi = fp16(ah[i] * s[i]) with ah = fp16(a) (packed
-// fp16 multiply), lo = fp16(a[i] * s[i] - hi[i]) with the residual formed by one
-// fused fp32 operation. Mixed-precision fused forms that round straight to fp16
-// are several times slower on this hardware than these.
+// hi + lo = x to about 21 bits: hi = fp16(ah[i] * s[i]) with ah an fp16 copy of a
+// (packed fp16 multiply), lo = fp16(a[i] * s[i] - hi[i]) with the residual formed by
+// one fused fp32 operation (so hi may be any nearby fp16 value). Mixed-precision
+// fused forms that round straight to fp16 are several times slower on this hardware
+// than these; the empty asm keeps the compiler from forming them.
 __device__ inline void split_products(const float* a, const half8& ah, const half8& s, half8& hi, half8& lo) {
   hi = ah * s;
   for (int i = 0; i < 8; i += 2) {
-    float l0 = __builtin_fmaf(a[i], float(s[i]), -float(hi[i]));
-    float l1 = __builtin_fmaf(a[i + 1], float(s[i + 1]), -float(hi[i + 1]));
-    asm("" : "+v"(l0), "+v"(l1));
-    lo[i] = _Float16(l0);
-    lo[i + 1] = _Float16(l1);
+    const float l0 = __builtin_fmaf(a[i], float(s[i]), -float(hi[i]));
+    const float l1 = __builtin_fmaf(a[i + 1], float(s[i + 1]), -float(hi[i + 1]));
+    float m0 = l0, m1 = l1;
+    asm("" : "+v"(m0), "+v"(m1));
+    lo[i] = _Float16(m0);
+    lo[i + 1] = _Float16(m1);
   }
 }
 
+// Low parts round to nearest even: their rounding errors, unlike those of a
+// truncation, do not share a sign and so do not add up over many tokens.
+__device__ inline half8 to_half8_rne(const float* a) {
+  half8 r;
+  for (int i = 0; i < 8; i += 2) {
+    float m0 = a[i], m1 = a[i + 1];
+    asm("" : "+v"(m0), "+v"(m1));  // keeps the conversion a plain packed one
+    r[i] = _Float16(m0);
+    r[i + 1] = _Float16(m1);
+  }
+  return r;
+}
+
+// fp16 copies that serve as high parts (of q, p, rotated keys), rounded toward zero
+// by the one-instruction packed conversion: whatever the high part misses, the low
+// part computed from it carries.
 __device__ inline half8 to_half8(const float* a) {
   half8 r;
-  for (int i = 0; i < 8; i++) r[i] = _Float16(a[i]);
+  for (int i = 0; i < 8; i += 2) {
+    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(a[i], a[i + 1]));
+    r[i] = h[0];
+    r[i + 1] = h[1];
+  }
   return r;
 }
 
@@ -610,7 +632,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const float exp_ = partner<U>(exh);
     ex = ishi ? exh : exp_;
   }
-  // q = qh16 + ql16 to about 22 bits (fp16 high part and fp16 residual)
+  // q = qh16 + ql16 to about 21 bits (fp16 high part and fp16 residual)
   half8 qh16[ITEMS], ql16[ITEMS];
   for (int it = 0; it < ITEMS; it++) {
     qh16[it] = to_half8(qreg[it]);
@@ -701,7 +723,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         const float* it = ropein + (16 * tile + lane % 16) * kD;
         const half8 ca = code_operand<BITS>(g.kc0, g.kc1, 2 * kc + tile);
         const half8 cb = code_operand<BITS>(g.kc0, g.kc1, 2 * (kc + 2) + tile);
-        half8 ah, al, bh, bl;
+        float ya[8], yb[8];
         for (int s2 = 0; s2 < 8; s2++) {
           const float bc = bcs[f0 + s2], bs = bcs[64 + f0 + s2];
           const float ci = it[f0 + s2], si = it[64 + f0 + s2];
@@ -709,13 +731,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
           const float sn = bs * ci + bc * si;
           const float xa = __builtin_fmaf(float(ca[s2]), float(sa[s2]), float(za[s2]));
           const float xb = __builtin_fmaf(float(cb[s2]), float(sb[s2]), float(zb[s2]));
-          const float ya = xa * c - xb * sn;
-          const float yb = xb * c + xa * sn;
-          ah[s2] = _Float16(ya);
-          al[s2] = _Float16(ya - float(ah[s2]));
-          bh[s2] = _Float16(yb);
-          bl[s2] = _Float16(yb - float(bh[s2]));
+          ya[s2] = xa * c - xb * sn;
+          yb[s2] = xb * c + xa * sn;
         }
+        // fp16 high parts (round toward zero) and the fp32 residuals as low parts
+        const half8 ah = to_half8(ya), bh = to_half8(yb);
+        float ra[8], rb[8];
+        for (int s2 = 0; s2 < 8; s2++) {
+          ra[s2] = ya[s2] - float(ah[s2]);
+          rb[s2] = yb[s2] - float(bh[s2]);
+        }
+        const half8 al = to_half8_rne(ra), bl = to_half8_rne(rb);
         float4v r = tile == 0 ? r0 : r1;
         r = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bka, r, 0, 0, 0);
         r = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bka, r, 0, 0, 0);
