@@ -632,6 +632,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const float exp_ = partner<U>(exh);
     ex = ishi ? exh : exp_;
   }
+  // Pre-RoPE keys at up to 4 query heads per kv-head: q of the channel 64 away
+  // (lane ^ 32), negated on the lanes that hold the upper channel of a rotary pair.
+  // (At 8 heads the query stays unrotated and the keys take the whole angle: the
+  // per-group query rotation would not fit in two waves' registers.)
+  constexpr bool QROT = ROPE && ITEMS == 1;
+  float qpair[8];
+  if constexpr (QROT) {
+    for (int e = 0; e < 8; e++) {
+      const float x = __shfl_xor(qreg[0][e], 32);
+      qpair[e] = cb < 8 ? x : -x;
+    }
+  }
   // q = qh16 + ql16 to about 21 bits (fp16 high part and fp16 residual)
   half8 qh16[ITEMS], ql16[ITEMS];
   for (int it = 0; it < ITEMS; it++) {
@@ -694,13 +706,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   };
 
   // Pre-RoPE keys: scores of the group's 32 tokens from the dequantized keys
-  // z + s * c rotated at their positions. Lane (token i, k-block kb) holds channels
-  // 32 kc + 8 kb + slot for kc = 0..3, so the rotary pair (f, f + 64) of its channel
-  // f < 64 sits in operand kc + 2 of the same lane and slot. The rotated key is
-  // split into fp16 high and low parts, two MFMAs each against B = q (high / low
-  // columns, staged once). The group's scale / zero-point region and its start
-  // angle's cos / sin come through this wave's shared memory; the in-group angle
-  // from the workgroup's table.
+  // z + s * c rotated at their positions n0 + i (n0 = the group's start). The
+  // rotation by n0 moves to the query: q . R(n0 + i) k = (R(-n0) q) . R(i) k, so B
+  // is R(-n0) q (fp16 high / low columns, staged per group like the plain key
+  // operand) and the keys turn by the in-group angles i * theta only, read from the
+  // workgroup's table. Lane (token i, k-block kb) holds channels 32 kc + 8 kb + slot
+  // for kc = 0..3, so the rotary pair (f, f + 64) of its channel f < 64 sits in
+  // operand kc + 2 of the same lane and slot. The rotated key is split into fp16
+  // high and low parts, two MFMAs each. The group's scale / zero-point region and
+  // its start angle's cos / sin come through this wave's shared memory.
   auto key_rope = [&](const GroupRegs<BITS, NJ>& g, float4v& r0, float4v& r1) {
     uint4* wl = ropew + wave * 64;
     wl[lane] = __builtin_bit_cast(uint4, g.ks);
@@ -709,6 +723,33 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint8_t* wb = reinterpret_cast<const uint8_t*>(wl);
     const float* bcs = reinterpret_cast<const float*>(wb + 512);  // cos[64] | sin[64] of the start
+    if constexpr (QROT) {
+      // R(-n0) q on this lane's key-operand slots: channel 8 cb + s pairs with the
+      // channel 64 away (held by lane ^ 32, whose q is qpair, sign folded in)
+      const int fq = 8 * (cb % 8);
+      const float4 c0 = *reinterpret_cast<const float4*>(bcs + fq);
+      const float4 c1 = *reinterpret_cast<const float4*>(bcs + fq + 4);
+      const float4 n0 = *reinterpret_cast<const float4*>(bcs + 64 + fq);
+      const float4 n1 = *reinterpret_cast<const float4*>(bcs + 64 + fq + 4);
+      const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sn[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+      for (int it = 0; it < ITEMS; it++) {
+        const int hh = hh0 + 4 * it;
+        float qr[8], rr[8];
+        for (int e = 0; e < 8; e++) qr[e] = __builtin_fmaf(qpair[e], sn[e], qreg[it][e] * cs[e]);
+        const half8 hi = to_half8(qr);
+        for (int e = 0; e < 8; e++) rr[e] = qr[e] - float(hi[e]);
+        const half8 lo = to_half8_rne(rr);
+        if (bwriter) {
+          const int rot = (U / 2) * (cb % 4);
+          sh.bk[wave].b[cb / 4][cb % 4][(hh + rot) % U] = hi;
+          sh.bk[wave].b[cb / 4][cb % 4][(U - 1 - hh + rot) % U] = lo;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     r0 = float4v{0.0f, 0.0f, 0.0f, 0.0f};
     r1 = r0;
     for (int kc = 0; kc < 2; kc++) {
@@ -725,10 +766,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         const half8 cb = code_operand<BITS>(g.kc0, g.kc1, 2 * (kc + 2) + tile);
         float ya[8], yb[8];
         for (int s2 = 0; s2 < 8; s2++) {
-          const float bc = bcs[f0 + s2], bs = bcs[64 + f0 + s2];
           const float ci = it[f0 + s2], si = it[64 + f0 + s2];
-          const float c = bc * ci - bs * si;
-          const float sn = bs * ci + bc * si;
+          float c = ci, sn = si;  // in-group angle; with QROT the start angle is in B
+          if constexpr (!QROT) {
+            const float bc = bcs[f0 + s2], bs = bcs[64 + f0 + s2];
+            c = bc * ci - bs * si;
+            sn = bs * ci + bc * si;
+          }
           const float xa = __builtin_fmaf(float(ca[s2]), float(sa[s2]), float(za[s2]));
           const float xb = __builtin_fmaf(float(cb[s2]), float(sb[s2]), float(zb[s2]));
           ya[s2] = xa * c - xb * sn;
@@ -859,7 +903,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       value_mfma(Gr);
     }
   };
-  if constexpr (ROPE) {
+  if constexpr (ROPE && !QROT) {
     // B = q for every group: the high / low split of q times a unit scale.
     GroupRegs<BITS, NJ> unit;
     for (int e = 0; e < 8; e++) {
