@@ -546,8 +546,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       G.vz[jr] = load_half8(blk + 2 * CB + 768 + 16 * (kb_ * 4 + jbase_ + jr));
     }
   };
-  // The first three groups' loads go out before the query is read, so that the two
-  // memory round trips overlap.
+  // The query entries this lane needs go out first (a few hundred bytes that every
+  // workgroup of the kv-head reads, so mostly cache hits), then the first three
+  // groups' loads: the query can be prepared as soon as it arrives and the first
+  // group computed as soon as its own loads land.
+  half8 qraw[ITEMS];
+  if (!tail && !a.rotate) {
+    for (int it = 0; it < ITEMS; it++)
+      qraw[it] = load_half8(reinterpret_cast<const uint8_t*>(
+          a.q + (size_t(b) * a.Hq + h * HG + (lane % 4) % HG + 4 * it) * kD + 8 * (lane / 4)));
+  }
   GroupRegs<BITS, NJ> R0, R1, R2, R3;
   if (n > 0) {
     load_group(0, R0);
@@ -611,8 +619,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   } else {
     float exo[ITEMS];
     for (int it = 0; it < ITEMS; it++) {
-      const half8 qh = load_half8(reinterpret_cast<const uint8_t*>(
-          a.q + (size_t(b) * a.Hq + h * HG + hh0 + 4 * it) * kD + 8 * cb));
+      const half8 qh = qraw[it];
       float m = 0.0f;
       for (int s = 0; s < 8; s++) {
         qreg[it][s] = float(qh[s]) * a.scale_log2;
