@@ -1,9 +1,11 @@
 // Decode-step attention read directly from the packed low-bit cache.
 //
-// Decode reads the whole cache at every step and is bound by memory traffic
-// ("Read What Matters", the NOVA-KV and RDKV abstracts; "KV cache quantization:
-// putting the bits in the cached vectors", the KIVI abstract on the compute core
-// idling while the cache loads). Scores over the quantized groups and over the FP16
+// Decode reads the whole cache at every step; the pages describe it as bound by
+// memory traffic ("Read What Matters", the NOVA-KV and RDKV abstracts; "KV cache
+// quantization: putting the bits in the cached vectors", the KIVI abstract on the
+// compute core idling while the cache loads). On gfx950 this kernel is bound by
+// instruction issue instead: per 32-token group a wave spends 64 code conversions
+// and 16 MFMAs on 3 KB of cache. Scores over the quantized groups and over the FP16
 // residual are combined inside one attention computation (same page, full-text-skim
 // notes on KIVI's grouped/residual split).
 //
@@ -13,12 +15,13 @@
 // second kernel merges them.
 //
 // Inside a split each wave streams whole 32-token groups straight into registers,
-// two groups ahead of the one it computes on. Every group block is read from HBM
-// once and serves all query heads of the kv-head:
+// issued three groups ahead of the group whose value side runs (two ahead of its
+// key side). Every group block is read from HBM once and serves all query heads of
+// the kv-head:
 //  * scores: an MFMA 16x16x32 f16 contraction over channels with the key codes as
 //    A (converted exactly to f16 by the scaled fp4/fp8 conversions) and, as B, the
 //    query multiplied by the group's per-channel key scale, split into fp16 high and
-//    low parts (two columns per head, so the product keeps ~22 bits); the key
+//    low parts (two columns per head, so the product keeps ~21 bits); the key
 //    zero-points enter through q.z, computed once per group per head;
 //  * values: an MFMA contraction over the group's tokens with the value codes as A
 //    and, as B, the softmax weight times the per-token value scale (again high/low
