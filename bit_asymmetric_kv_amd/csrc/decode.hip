@@ -479,7 +479,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     split = nsb + (int(blockIdx.x) - wbase) % a.wblocks;
   } else {
     const int idx = int(blockIdx.x);
-    if (!a.plan.use_prefix) {
+    if (a.plan.older_weight > 0.0f) {
+      // split-major: equal split counts for every sequence (one round)
+      nsb = a.plan.use_prefix ? a.plan.count[a.plan.seq[0]] : a.plan.uniform;
+      const int bh = idx % (a.B * a.Hkv);
+      split = idx / (a.B * a.Hkv);
+      b = a.plan.use_prefix ? a.plan.seq[bh / a.Hkv] : bh / a.Hkv;
+      h = bh % a.Hkv;
+    } else if (!a.plan.use_prefix) {
       nsb = a.plan.uniform;
       b = idx / (a.Hkv * nsb);
       const int rem = idx - b * a.Hkv * nsb;
@@ -505,8 +512,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int ng = Q / kG;
 
   // This wave's groups.
-  const int g0 = split * a.gps;
-  const int g1 = min(ng, g0 + a.gps);
+  int g0 = split * a.gps, g1 = min(ng, g0 + a.gps);
+  if (a.plan.older_weight > 0.0f && !tail) {
+    // splits [0, nold) take older_weight times the groups of splits [nold, nsb)
+    const int nold = (nsb + 1) / 2;
+    const float w = a.plan.older_weight;
+    const float x = float(ng) / (float(nold) + float(nsb - nold) / w);
+    auto bound = [&](int sp) {
+      const float v = sp <= nold ? float(sp) * x : float(nold) * x + float(sp - nold) * (x / w);
+      return min(ng, int(v + 0.5f));
+    };
+    g0 = bound(split);
+    g1 = split == nsb - 1 ? ng : bound(split + 1);
+  }
   const int len = tail ? 0 : max(0, g1 - g0);
   const int per = (len + kWaves - 1) / kWaves;
   // wave-uniform (kept in scalar registers: a paged cache's table entries are then
@@ -1032,14 +1050,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
 
 template <int BITS, int HG, bool ROPE>
 int resident_blocks_of() {
-  int dev = 0, per_cu = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<BITS, HG, ROPE>, 256, 0) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<BITS, HG, ROPE>, 256, 0) !=
+      hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
-  return per_cu * cus;
+  return per_cu;
 }
 
 template <int BITS, int HG, bool ROPE>
@@ -1095,8 +1112,18 @@ int resident_blocks_for(int bits, int hg) {
          : hg == 4 ? resident_blocks_of<4, 4, ROPE>() : resident_blocks_of<4, 8, ROPE>();
 }
 
-int decode_resident_blocks(int bits, int hg, int rope) {
+int decode_blocks_per_cu(int bits, int hg, int rope) {
   return rope ? resident_blocks_for<true>(bits, hg) : resident_blocks_for<false>(bits, hg);
+}
+
+int device_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return cus;
 }
 
 template <bool ROPE>

@@ -144,7 +144,8 @@ struct kvq_cache {
   std::vector<int64_t> T, Q;
   int32_t groups_per_split = 0;
   hipEvent_t prof_start = nullptr, prof_stop = nullptr;
-  int resident_blocks = 0;
+  int resident_blocks = 0;  // decode split workgroups that fit on the device at once
+  int blocks_per_cu = 0;
   SeqDesc* staging[kStaging] = {};
   hipEvent_t staging_done[kStaging] = {};
   int next_staging = 0;
@@ -648,9 +649,11 @@ kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const 
     // workgroups, each reading about the same number of groups, so a sequence gets
     // splits in proportion to its length. With unequal lengths the splits are made
     // three times finer, so that the last splits of the sequences even out.
-    if (c->resident_blocks == 0)
-      c->resident_blocks = std::max(1, kvq::decode_resident_blocks(
-                                            c->cfg.bits, c->cfg.num_q_heads / c->cfg.num_kv_heads, c->cfg.rope));
+    if (c->resident_blocks == 0) {
+      c->blocks_per_cu = kvq::decode_blocks_per_cu(c->cfg.bits, c->cfg.num_q_heads / c->cfg.num_kv_heads,
+                                                   c->cfg.rope);
+      c->resident_blocks = std::max(1, c->blocks_per_cu * kvq::device_compute_units());
+    }
     const int64_t win = int64_t(B) * Hkv * c->L.win_blocks;
     const int64_t slots = std::max<int64_t>(int64_t(B) * Hkv,
                                             c->resident_blocks - std::min<int64_t>(win, c->resident_blocks / 4));
@@ -683,6 +686,16 @@ kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const 
     plan.uniform = int32_t(max_split);
   }
   plan.pstride = int32_t(max_split) + c->L.win_blocks;
+  // One round of equal sequences at two workgroups per compute unit: the dispatcher
+  // fills every compute unit's first slot before its second, and a compute unit then
+  // issues from its older workgroup first, so the younger one trails and ends alone.
+  // Giving the first-dispatched half of the splits twice the groups of the second half
+  // lets both end together (measured at 128K tokens: 7 % shorter steps). Explicit
+  // split sizes keep equal splits.
+  plan.older_weight = 0.0f;
+  if (c->groups_per_split == 0 && uniform_lengths && c->blocks_per_cu == 2 && max_split >= 2 &&
+      max_split * int64_t(B) * Hkv + int64_t(B) * Hkv * c->L.win_blocks <= c->resident_blocks)
+    plan.older_weight = 2.0f;
   const float scale_log2 = c->cfg.softmax_scale * 1.4426950408889634f;
   const SeqDesc* dev_seq = reinterpret_cast<const SeqDesc*>(c->base + c->L.seq_off);
   kvq::AppendArgs app{};

@@ -59,6 +59,12 @@ struct AppendArgs {
 // prefix[p] = n_seq[0] + ... + n_seq[p-1]; count[b] = n_b. Otherwise every sequence
 // has n_b = uniform, in index order. Partials of (sequence, query head) sit at
 // `pstride` slots: n_b splits, then the FP16 window's.
+//
+// With `older_weight` > 0 (one round of equal sequences, two workgroups per compute
+// unit) the grid is split-major: the first half of the split workgroups, which the
+// dispatcher places first on every compute unit and which then get its issue
+// priority, are the lower half of every head's splits, and each of them takes
+// older_weight times the groups of a split in the upper half.
 struct SplitPlan {
   int32_t prefix[kInlineSeqs + 1];
   int32_t seq[kInlineSeqs];
@@ -66,6 +72,7 @@ struct SplitPlan {
   int32_t use_prefix;
   int32_t uniform;
   int32_t pstride;
+  float older_weight;
 };
 
 // Where the packed group blocks live. Contiguous caches: [B][Hkv][gcap][GB].
@@ -128,8 +135,10 @@ hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqArgs& seq, cons
 hipError_t launch_ring_write(const Layout& L, uint8_t* base, const SeqArgs& seq, const void* k,
                              const void* v, int32_t n_max, int32_t max_ring_tokens, int rotate,
                              hipStream_t stream);
-// Workgroups of the decode split kernel that fit on the current device at once.
-int decode_resident_blocks(int bits, int hg, int rope);
+// Workgroups of the decode split kernel that fit on one compute unit of the current
+// device at once, and the device's compute units.
+int decode_blocks_per_cu(int bits, int hg, int rope);
+int device_compute_units();
 hipError_t launch_rope_tables(const Layout& L, uint8_t* base, double rope_base, hipStream_t stream);
 hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const AppendArgs& app,
                          const void* q, float* out, int32_t groups_per_split, const SplitPlan& plan,
