@@ -424,7 +424,7 @@ struct GroupRegs {
 };
 
 template <int BITS, int HG, bool ROPE>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, (BITS == 4 && ROPE && HG <= 4) ? 2 : 1) void decode_split_kernel(DecodeArgs a) {
   // MFMA columns. Key side: U = 2 * HG column kinds, the fp16 high part of head u at
   // u < HG and the low part of head U - 1 - u at u >= HG (u = column % U), repeated
   // over the 16 columns; the two parts of a score are added across the paired
@@ -664,7 +664,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // (lane ^ 32), negated on the lanes that hold the upper channel of a rotary pair.
   // (At 8 heads the query stays unrotated and the keys take the whole angle: the
   // per-group query rotation would not fit in two waves' registers.)
-  constexpr bool QROT = ROPE && ITEMS == 1;
+  constexpr bool QROT = ROPE && ITEMS == 1 && BITS != 4;
   float qpair[8];
   if constexpr (QROT) {
     for (int e = 0; e < 8; e++) {
@@ -672,12 +672,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       qpair[e] = cb < 8 ? x : -x;
     }
   }
-  // q = qh16 + ql16 to about 21 bits (fp16 high part and fp16 residual)
-  half8 qh16[ITEMS], ql16[ITEMS];
-  for (int it = 0; it < ITEMS; it++) {
-    qh16[it] = to_half8(qreg[it]);
-    for (int e = 0; e < 8; e++) ql16[it][e] = _Float16(qreg[it][e] - float(qh16[it][e]));
-  }
+  // q = qh16 + ql16 to about 21 bits (fp16 high part and fp16 residual); the
+  // residual is kept for one query item per lane only (two would not fit in two
+  // waves' registers, and their low parts come from the fp32 query instead)
+  half8 qh16[ITEMS], ql16[ITEMS == 1 ? 1 : 1];
+  for (int it = 0; it < ITEMS; it++) qh16[it] = to_half8(qreg[it]);
+  if constexpr (ITEMS == 1)
+    for (int e = 0; e < 8; e++) ql16[0][e] = _Float16(qreg[0][e] - float(qh16[0][e]));
 
   float4v oacc[8];
   for (int t = 0; t < 8; t++) oacc[t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -699,11 +700,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int it = 0; it < ITEMS; it++) {
       const int hh = hh0 + 4 * it;
       half8 hi, lo;
-      // hi = fp16(qh * s); qh * s - hi is exact in fp16 (the rounding error of a
-      // product), so one fused fp16 operation forms it and a second adds ql * s
-      hi = qh16[it] * g.ks;
-      lo = __builtin_elementwise_fma(qh16[it], g.ks, -hi);
-      lo = __builtin_elementwise_fma(ql16[it], g.ks, lo);
+      if constexpr (ITEMS == 1) {
+        // hi = fp16(qh * s); qh * s - hi is exact in fp16 (the rounding error of a
+        // product), so one fused fp16 operation forms it and a second adds ql * s
+        hi = qh16[it] * g.ks;
+        lo = __builtin_elementwise_fma(qh16[it], g.ks, -hi);
+        lo = __builtin_elementwise_fma(ql16[0], g.ks, lo);
+      } else {
+        split_products(qreg[it], qh16[it], g.ks, hi, lo);
+      }
       float z = 0.0f;
       for (int s = 0; s < 8; s++) z = __builtin_fmaf(qreg[it][s], float(g.kz[s]), z);
       qz[it] = wave_sum_rows(row_sum_stride4(z));
