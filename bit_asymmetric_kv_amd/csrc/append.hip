@@ -107,16 +107,28 @@ __device__ inline QuantOut quantize_regs(const float* x, uint8_t* codes) {
   return {s16, z16};
 }
 
-template <int BITS>
+// ROT: keys are Walsh-Hadamard rotated (a template parameter, so that the rotation's
+// registers do not lower the occupancy of the plain kernel).
+template <int BITS, bool ROT>
 __global__ __launch_bounds__(64) void flush_wave_kernel(const GroupStore store, const __half* __restrict__ ringk,
                                                         const __half* __restrict__ ringv, const SeqArgs seq,
                                                         const __half* __restrict__ kin,
                                                         const __half* __restrict__ vin, int Hkv, int W, int RS,
-                                                        int sink, int n_max, int rotate) {
+                                                        int sink, int n_max) {
   constexpr int CB = kG * kD * BITS / 8;  // bytes of one code section
   constexpr int GB = 2 * CB + 1024;
-  __shared__ uint8_t ck[kG][kD];  // key codes [token][channel]
-  __shared__ uint8_t cv[kG][kD];  // value codes [token][channel]
+  // key and value codes [token][channel]; with rotation the same bytes first hold the
+  // rotated keys [token][channel] on their way to the per-channel layout
+  __shared__ union {
+    struct {
+      uint8_t ck[kG][kD];
+      uint8_t cv[kG][kD];
+    } c;
+    __half kt[kG][kD];
+  } sm;
+  auto& ck = sm.c.ck;
+  auto& cv = sm.c.cv;
+  auto& kt = sm.kt;
   __shared__ __half vsz[2][kD];   // value scales / zero-points in block order
 
   const int lane = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -134,9 +146,16 @@ __global__ __launch_bounds__(64) void flush_wave_kernel(const GroupStore store, 
   uint8_t* blk = store.at(b, h, g);
 
   // Every load of the group is issued before any arithmetic: 32 key words (channels
-  // 2l, 2l+1 of each token) and the lane's two 64-byte value segments.
+  // 2l, 2l+1 of each token; with rotation, lane l takes half l % 2 of token l / 2
+  // instead) and the lane's two 64-byte value segments.
   uint32_t ku[kG];
-  for (int i = 0; i < kG; i++) ku[i] = *reinterpret_cast<const uint32_t*>(row(ringk, kin, t0 + i) + 2 * lane);
+  uint4 kr[8];
+  if constexpr (ROT) {
+    const uint4* src = reinterpret_cast<const uint4*>(row(ringk, kin, t0 + lane / 2) + 64 * (lane % 2));
+    for (int q = 0; q < 8; q++) kr[q] = src[q];
+  } else {
+    for (int i = 0; i < kG; i++) ku[i] = *reinterpret_cast<const uint32_t*>(row(ringk, kin, t0 + i) + 2 * lane);
+  }
   uint4 vu[2][4];
   for (int k = 0; k < 2; k++) {
     const uint4* src = reinterpret_cast<const uint4*>(row(ringv, vin, t0 + 16 * k + lane / 4) + kG * (lane % 4));
@@ -146,29 +165,52 @@ __global__ __launch_bounds__(64) void flush_wave_kernel(const GroupStore store, 
   // Keys.
   {
     float x0[kG], x1[kG];
-    for (int i = 0; i < kG; i++) {
-      x0[i] = __half2float(__ushort_as_half(static_cast<unsigned short>(ku[i] & 0xFFFFu)));
-      x1[i] = __half2float(__ushort_as_half(static_cast<unsigned short>(ku[i] >> 16)));
-    }
-    if (rotate) {
-      for (int i = 0; i < kG; i++) {
-        if (t0 + i < sd.t_old) continue;  // window rows are stored rotated already
-        float a = x0[i], c = x1[i];
-        float p0 = a + c, p1 = a - c;  // half-width 1: channels 2l, 2l + 1
-        for (int m = 1; m < kD / 2; m <<= 1) {  // half-width 2m: partner lane l ^ m
-          const float q0 = __shfl_xor(p0, m), q1 = __shfl_xor(p1, m);
-          if ((lane & m) == 0) {
-            p0 = p0 + q0;
-            p1 = p1 + q1;
-          } else {
-            p0 = q0 - p0;
-            p1 = q1 - p1;
-          }
+    if constexpr (ROT) {
+      // Lane l rotates half l % 2 (channels 64 (l % 2) ...) of token t0 + l / 2: the
+      // butterflies of half-width 1 ... 32 stay in its registers, half-width 64 pairs
+      // it with lane l ^ 1; the rounded keys go through shared memory back to the
+      // per-channel layout. Window rows are stored rotated already.
+      const int tl = lane / 2, hf = lane % 2;
+      float y[64];
+      for (int q = 0; q < 8; q++) {
+        const uint32_t w[4] = {kr[q].x, kr[q].y, kr[q].z, kr[q].w};
+        for (int e = 0; e < 4; e++) {
+          y[8 * q + 2 * e] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[e] & 0xFFFFu)));
+          y[8 * q + 2 * e + 1] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[e] >> 16)));
         }
-        float y0 = p0 * kInvSqrt128, y1 = p1 * kInvSqrt128;
-        asm volatile("" : "+v"(y0), "+v"(y1));  // round the product to fp32 first
-        x0[i] = __half2float(__float2half_rn(y0));
-        x1[i] = __half2float(__float2half_rn(y1));
+      }
+      if (t0 + tl >= sd.t_old) {  // the partner lane (same token) takes the same branch
+        for (int hw = 1; hw < 64; hw <<= 1)
+          for (int j = 0; j < 64; j += 2 * hw)
+            for (int k = j; k < j + hw; k++) {
+              const float a = y[k], c = y[k + hw];
+              y[k] = a + c;
+              y[k + hw] = a - c;
+            }
+        for (int k = 0; k < 64; k++) {
+          const float o = __builtin_bit_cast(
+              float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y[k]), 0xB1, 0xF, 0xF, false));
+          y[k] = hf == 0 ? y[k] + o : o - y[k];  // (channel c, c + 64) -> (sum, difference)
+        }
+        for (int k = 0; k < 64; k++) {
+          float v = y[k] * kInvSqrt128;
+          asm volatile("" : "+v"(v));  // round the product to fp32 first
+          y[k] = __half2float(__float2half_rn(v));
+        }
+      }
+      for (int k = 0; k < 64; k += 2)
+        *reinterpret_cast<__half2*>(&kt[tl][64 * hf + k]) = __floats2half2_rn(y[k], y[k + 1]);
+      __syncthreads();
+      for (int i = 0; i < kG; i++) {
+        const __half2 v = *reinterpret_cast<const __half2*>(&kt[i][2 * lane]);
+        x0[i] = __low2float(v);
+        x1[i] = __high2float(v);
+      }
+      __syncthreads();  // the key codes overwrite these bytes next
+    } else {
+      for (int i = 0; i < kG; i++) {
+        x0[i] = __half2float(__ushort_as_half(static_cast<unsigned short>(ku[i] & 0xFFFFu)));
+        x1[i] = __half2float(__ushort_as_half(static_cast<unsigned short>(ku[i] >> 16)));
       }
     }
     uint8_t c0[kG], c1[kG];
@@ -327,15 +369,20 @@ hipError_t launch_flush(const Layout& L, uint8_t* base, const SeqArgs& seq, cons
   auto* rv = reinterpret_cast<const __half*>(base + L.ringv_off);
   auto* kin = static_cast<const __half*>(k);
   auto* vin = static_cast<const __half*>(v);
-  if (L.bits == 2)
-    hipLaunchKernelGGL(flush_wave_kernel<2>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
-                       L.RS, L.sink, n_max, rotate);
-  else if (L.bits == 3)
-    hipLaunchKernelGGL(flush_wave_kernel<3>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
-                       L.RS, L.sink, n_max, rotate);
-  else
-    hipLaunchKernelGGL(flush_wave_kernel<4>, grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, L.W,
-                       L.RS, L.sink, n_max, rotate);
+#define KVQ_FLUSH(BITS, ROT)                                                                                  \
+  hipLaunchKernelGGL((flush_wave_kernel<BITS, ROT>), grid, dim3(64), 0, stream, blocks, rk, rv, seq, kin, vin, L.Hkv, \
+                     L.W, L.RS, L.sink, n_max)
+  if (L.bits == 2) {
+    if (rotate) KVQ_FLUSH(2, true);
+    else KVQ_FLUSH(2, false);
+  } else if (L.bits == 3) {
+    if (rotate) KVQ_FLUSH(3, true);
+    else KVQ_FLUSH(3, false);
+  } else {
+    if (rotate) KVQ_FLUSH(4, true);
+    else KVQ_FLUSH(4, false);
+  }
+#undef KVQ_FLUSH
   return hipGetLastError();
 }
 
