@@ -60,7 +60,8 @@ class Workload:
         return replace(self, **kw)
 
 
-# The five workloads: shapes, bit widths, window sizes and key distributions.
+# The workloads: the five configurations (the 128K one at 2, 3 and 4 bits) and two
+# variants of the 128K shape; shapes, bit widths, window sizes and key distributions.
 WORKLOADS = {
     "tiny_mha_4k": Workload("tiny_mha_4k", 1, 8, 8, 4096, 1, 2, 32, 32, False, 4, 10.0, 0.0, 1001),
     "llama2_7b_b8_32k": Workload("llama2_7b_b8_32k", 8, 32, 32, 32768, 64, 2, 32, 128, False, 8, 8.0, 0.0, 1002),
@@ -73,6 +74,8 @@ WORKLOADS = {
     # the headline shape with pre-RoPE keys and an attention sink
     "gqa_128k_2bit_rope": Workload("gqa_128k_2bit_rope", 1, 32, 8, 131072, 1, 2, 32, 128, False, 4, 10.0, 3.0,
                                    1006, sink=True, rope=True),
+    # the headline context with 8 query heads per KV head (64 / 8, a 70B-class layer)
+    "gqa_128k_2bit_hg8": Workload("gqa_128k_2bit_hg8", 1, 64, 8, 131072, 1, 2, 32, 128, False, 4, 10.0, 3.0, 1007),
 }
 
 

@@ -109,6 +109,11 @@ def test_full_gqa_128k(dev, name):
     _run_full(wl.WORKLOADS[name], dev, [(0, 0), (0, 5)], 1, {0})
 
 
+def test_full_gqa_128k_hg8(dev):
+    # 8 query heads per KV head: a column kind per head and part, no copies
+    _run_full(wl.WORKLOADS["gqa_128k_2bit_hg8"], dev, [(0, 2), (0, 7)], 1, {0})
+
+
 def test_full_million_1m(dev):
     sample = lambda ng: list(range(0, ng, 97)) + list(range(ng - 40, ng))
     _run_full(wl.WORKLOADS["million_1m"], dev, [(0, 3)], 1, {0}, group_sample=sample)
