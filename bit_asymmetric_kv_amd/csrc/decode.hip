@@ -668,7 +668,7 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
   // (lane ^ 32), negated on the lanes that hold the upper channel of a rotary pair.
   // (At 8 heads the query stays unrotated and the keys take the whole angle: the
   // per-group query rotation would not fit in two waves' registers.)
-  constexpr bool QROT = ROPE && ITEMS == 1 && BITS != 4;
+  constexpr bool QROT = ROPE && ITEMS == 1;
   float qpair[8];
   if constexpr (QROT) {
     for (int e = 0; e < 8; e++) {
