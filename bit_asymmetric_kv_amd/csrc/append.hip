@@ -116,7 +116,6 @@ __global__ __launch_bounds__(64) void flush_wave_kernel(const GroupStore store, 
                                                         const __half* __restrict__ vin, int Hkv, int W, int RS,
                                                         int sink, int n_max) {
   constexpr int CB = kG * kD * BITS / 8;  // bytes of one code section
-  constexpr int GB = 2 * CB + 1024;
   // key and value codes [token][channel]; with rotation the same bytes first hold the
   // rotated keys [token][channel] on their way to the per-channel layout
   __shared__ union {

@@ -176,21 +176,23 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes) {
 
 void kvq_destroy(kvq_cache* c) {
   if (!c) return;
-  hipSetDevice(c->device);
-  hipStreamSynchronize(c->create_stream);
+  // Best-effort teardown: there is no status to return, so a failing call does not
+  // stop the release of what remains.
+  (void)hipSetDevice(c->device);
+  (void)hipStreamSynchronize(c->create_stream);
   for (int i = 0; i < kStaging; i++) {
     if (c->staging_done[i]) {
-      hipEventSynchronize(c->staging_done[i]);
-      hipEventDestroy(c->staging_done[i]);
+      (void)hipEventSynchronize(c->staging_done[i]);
+      (void)hipEventDestroy(c->staging_done[i]);
     }
-    if (c->staging[i]) hipHostFree(c->staging[i]);
+    if (c->staging[i]) (void)hipHostFree(c->staging[i]);
   }
   if (c->table_done) {
-    hipEventSynchronize(c->table_done);
-    hipEventDestroy(c->table_done);
+    (void)hipEventSynchronize(c->table_done);
+    (void)hipEventDestroy(c->table_done);
   }
-  if (c->table) hipHostFree(c->table);
-  if (c->owned && c->base) hipFree(c->base);
+  if (c->table) (void)hipHostFree(c->table);
+  if (c->owned && c->base) (void)hipFree(c->base);
   delete c;
 }
 
@@ -218,7 +220,11 @@ kvq_status kvq_create(const kvq_config* cfg, void* dev_mem, size_t dev_bytes, hi
   c->create_stream = stream;
   c->T.assign(cfg->batch, 0);
   c->Q.assign(cfg->batch, 0);
-  hipGetDevice(&c->device);
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    (void)hipGetLastError();
+    delete c;
+    return fail(KVQ_ERR_NO_DEVICE, "no current HIP device");
+  }
   if (dev_mem) {
     c->base = static_cast<uint8_t*>(dev_mem);
   } else {
