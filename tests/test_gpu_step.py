@@ -120,3 +120,47 @@ def test_step_on_empty_sequence_fails_and_changes_nothing(dev):
     out = cache.step(k, k, q)
     torch.cuda.synchronize()
     assert cache.seq_len(0) == (3, 0) and bool(torch.isfinite(out).all())
+
+
+def test_library_allocated_cache_matches_caller_memory(dev):
+    """kvq_create with dev_mem NULL: the library allocates the cache itself (and
+    frees it in kvq_destroy). Driven through the C ABI directly, it gives the same
+    outputs bit for bit as a cache in caller-provided memory fed the same inputs."""
+    import ctypes
+    import bit_asymmetric_kv_amd as kvq
+    from bit_asymmetric_kv_amd import _lib
+    lib = _lib.load()
+    w = wl.WORKLOADS["gqa_128k_2bit"]
+    B, ctx = w.batch, 1000
+    print(f"case library-allocated cache {w.name} ctx={ctx}", flush=True)
+    cfg = kvq.make_config(B, w.num_q_heads, w.num_kv_heads, residual=w.residual, max_tokens=ctx + 64)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    h = ctypes.c_void_p(0)
+    _lib.check(lib.kvq_create(ctypes.byref(cfg), None, 0, stream, ctypes.byref(h)))
+    assert h.value
+    ref = kvq.KVCache(B, w.num_q_heads, w.num_kv_heads, residual=w.residual, max_tokens=ctx + 64, device=dev)
+    try:
+        T = np.zeros(B, dtype=np.int64)
+        k, v = wl.kv_batch(w, T, ctx, np.full(B, ctx, dtype=np.int64))
+        kd, vd = to_dev(k, torch, dev), to_dev(v, torch, dev)
+        _lib.check(lib.kvq_append(h, kd.data_ptr(), vd.data_ptr(), None, ctx, stream))
+        ref.append(kd, vd)
+        T += ctx
+        for s in range(40):  # one token per step: crosses a group flush
+            k1, v1 = wl.kv_batch(w, T, 1, np.ones(B, dtype=np.int64))
+            k1d, v1d = to_dev(k1, torch, dev), to_dev(v1, torch, dev)
+            _lib.check(lib.kvq_append(h, k1d.data_ptr(), v1d.data_ptr(), None, 1, stream))
+            ref.append(k1d, v1d)
+            T += 1
+            qd = to_dev(wl.queries(w, s), torch, dev)
+            out = torch.empty(B, w.num_q_heads, 128, dtype=torch.float32, device=dev)
+            _lib.check(lib.kvq_decode_attention(h, qd.data_ptr(), out.data_ptr(), stream))
+            exp = ref.decode(qd)
+            torch.cuda.synchronize()
+            assert torch.equal(out, exp), f"step {s}: max diff {float((out - exp).abs().max()):.3e}"
+        tl, ql = ctypes.c_int64(0), ctypes.c_int64(0)
+        _lib.check(lib.kvq_seq_len(h, 0, ctypes.byref(tl), ctypes.byref(ql)))
+        assert (tl.value, ql.value) == ref.seq_len(0)
+    finally:
+        lib.kvq_destroy(h)
+        ref.close()
