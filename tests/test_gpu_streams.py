@@ -57,3 +57,47 @@ def test_side_stream_prefill_and_steps(dev, one_call):
     p.check_state()
     p.gpu.close()
     print(f"worst {worst:.3e}", flush=True)
+
+
+def test_two_caches_on_two_streams_interleaved(dev):
+    """Two caches of different shapes and widths (2-bit 32/8 heads, 4-bit 8/8 heads
+    with sink and pre-RoPE keys) stepped in turn on two side streams, with no
+    synchronization between their launches: each matches its own oracle, so the
+    library keeps no state shared between caches that their calls could race on."""
+    base = wl.WORKLOADS["gqa_128k_2bit"]
+    other = wl.Workload("mha_4bit_sink_rope", 2, 8, 8, 0, 0, 4, 32, 64, False, 2, 8.0, 2.0, 4242,
+                        sink=True, rope=True)
+    ctx, steps = 1200, 36
+    print(f"case two caches on two streams ctx={ctx} steps={steps}", flush=True)
+    main = torch.cuda.current_stream(dev)
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    pairs = []
+    for w, st in zip((base, other), streams):
+        with torch.cuda.stream(st):
+            p = Pair(w, ctx + steps + 8, dev, torch)
+            p.append([ctx] * w.batch)
+        pairs.append(p)
+    for s in range(steps):
+        outs = []
+        for p, st in zip(pairs, streams):
+            w = p.w
+            ones = np.ones(w.batch, dtype=np.int64)
+            k, v = wl.kv_batch(w, p.T, 1, ones)
+            q = wl.queries(w, s)
+            with torch.cuda.stream(st):
+                out = p.gpu.step(to_dev(k, torch, dev), to_dev(v, torch, dev), to_dev(q, torch, dev),
+                                 n_tokens=ones.tolist())
+            p.ref.append(k, v, ones)
+            p.T += ones
+            outs.append((p, out, q))
+        for st in streams:
+            main.wait_stream(st)
+        for p, out, q in outs:
+            got = out.cpu().numpy().astype(np.float64)
+            err = float(np.abs(got - p.ref.decode(q)).max())
+            assert np.all(np.isfinite(got)) and err <= OUT_TOL, f"{p.w.name} step {s}: max |gpu - oracle| = {err:.3e}"
+    for st in streams:
+        main.wait_stream(st)
+    for p in pairs:
+        p.check_state()
+        p.gpu.close()
