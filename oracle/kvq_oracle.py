@@ -448,10 +448,6 @@ class OracleHead:
         """Packed byte block of quantized group g."""
         return pack_group_block(*self.group(g), self.bits)
 
-    def ring_slot(self, t: int, ring_len: int) -> int:
-        """Slot of FP16 token t in a ring of ring_len = R + G slots."""
-        return t % ring_len
-
     def cache_values(self):
         """Keys and values as attention sees them: dequantized (float64) for the
         quantized tokens [o, o + Q), the stored fp16 values for the rest (the window

@@ -34,6 +34,48 @@ def test_hand_worked_cases(case):
     assert float(z16) == case["z16"]
 
 
+def test_clamp_cases_bind():
+    # The clamp_binds fixtures must really need the clamp: with the stored scale the
+    # rounded product of the group maximum lies above the top level (checked here in
+    # exact double arithmetic: every value is a small multiple of 2^-24).
+    cases = [c for c in _load("quantizer_cases.json")["cases"] if c.get("clamp_binds")]
+    assert {c["bits"] for c in cases} == {2, 3, 4}
+    for c in cases:
+        top = max(c["x"]) - c["z16"]
+        assert round(top / c["s16"]) > 2 ** c["bits"] - 1 or top / c["s16"] == 2 ** c["bits"] - 0.5
+        assert max(c["codes"]) == 2 ** c["bits"] - 1
+
+
+def test_dequantize_block_hand_computed():
+    # Per-channel key scales and per-(token, channel group) value scales that all
+    # differ, so a transposed or tiled scale array reads a different entry.
+    # Keys: ks[d] = d / 8, kz[d] = -d, kc[t, d] = (t + d) % 4.
+    # Values: vs[t, j] = (t + 1) / 4 + j, vz[t, j] = j - t, vc[t, d] = (3 t + d) % 4,
+    # channel d in group j = d // 32.
+    d = np.arange(128)
+    t = np.arange(32)[:, None]
+    ks = (d / 8).astype(np.float16)
+    kz = (-d).astype(np.float16)
+    kc = ((t + d[None, :]) % 4).astype(np.uint8)
+    j = np.arange(4)[None, :]
+    vs = ((t + 1) / 4 + j).astype(np.float16)
+    vz = (j - t).astype(np.float16)
+    vc = ((3 * t + d[None, :]) % 4).astype(np.uint8)
+    kh, vh = dequantize_block(kc, ks, kz, vc, vs, vz)
+    assert kh.shape == vh.shape == (32, 128)
+    # k[5, 70]: kc = 75 % 4 = 3, so -70 + (70 / 8) * 3 = -70 + 26.25 = -43.75
+    assert kh[5, 70] == -43.75
+    # k[31, 1]: kc = 32 % 4 = 0, so the zero-point -1 alone
+    assert kh[31, 1] == -1.0
+    # v[9, 100]: group 3, vs = 10 / 4 + 3 = 5.5, vz = 3 - 9 = -6, vc = 127 % 4 = 3:
+    # -6 + 16.5 = 10.5 (channel 100 % 4 = 0 would read group 0: -9 + 2.5 * 3 = -1.5)
+    assert vh[9, 100] == 10.5
+    # v[0, 33]: group 1, vs = 1.25, vz = 1, vc = 33 % 4 = 1: 2.25
+    assert vh[0, 33] == 2.25
+    # v[20, 31]: group 0, vs = 5.25, vz = -20, vc = 91 % 4 = 3: -20 + 15.75 = -4.25
+    assert vh[20, 31] == -4.25
+
+
 def _rand_groups(rng, n, bits):
     scale = rng.choice([1e-3, 1.0, 30.0, 1000.0], size=(n, 1))
     off = rng.standard_normal((n, 1)) * scale * 3
