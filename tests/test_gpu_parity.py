@@ -153,6 +153,14 @@ def _adversarial_groups():
     v[100, 32:64] = np.resize(np.array([0, tiny], dtype=np.float16), 32)
     k[128:160, 11] = np.resize(np.array([-65504, 65504], dtype=np.float16), 32)    # full fp16 range
     v[130, 64:96] = np.resize(np.array([-65504, 65504], dtype=np.float16), 32)
+    # subnormal ranges whose fp16 scale rounds below (max - min) / (2^b - 1), so the
+    # top code only stays in range through the clamp to 2^b - 1 (hand-worked in
+    # tests/golden/quantizer_cases.json): multiples n * 2^-24 of the smallest subnormal
+    for c, ns in zip(range(13, 19), ([0, 4, 3, 2, 1], [0, 7], [0, 10, 9, 8], [0, 15],
+                                     [0, 20, 17, 16, 15], [0, 31])):
+        grp = np.array(ns, dtype=np.float64) * 2.0 ** -24
+        k[96:128, c] = np.resize(grp.astype(np.float16), 32)
+        v[101 + c - 13, 32:64] = np.resize(grp.astype(np.float16), 32)
     return k, v
 
 
@@ -174,6 +182,9 @@ def test_adversarial_groups_bit_exact(dev, bits):
     exp = ref.attend(q.cpu().numpy()[0])[0]
     assert np.all(np.isfinite(out))
     assert np.max(np.abs(out - exp)) <= 2e-3 * max(1.0, np.abs(exp).max())
+    # channels that no +-65504 value feeds meet the plain bar
+    plain = np.r_[0:64, 96:128]
+    assert np.max(np.abs(out[plain] - exp[plain])) <= 2e-3
 
 
 def test_errors_leave_state_unchanged(dev):
