@@ -43,6 +43,8 @@ int64_t quantized_count(int64_t T, int64_t R, int sink) {
   return (over / kvq::kGroup) * kvq::kGroup;
 }
 
+Layout make_layout(const kvq_config* cfg);
+
 kvq_status validate(const kvq_config* cfg) {
   if (!cfg) return fail(KVQ_ERR_INVALID_ARG, "config is NULL");
   if (cfg->batch < 1) return fail(KVQ_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", cfg->batch);
@@ -80,6 +82,18 @@ kvq_status validate(const kvq_config* cfg) {
     return fail(KVQ_ERR_INVALID_ARG, "page_groups must be 0 or a power of two up to %d", kvq::kMaxPageGroups);
   if (cfg->page_groups > 0 && (cfg->pool_pages < 1 || cfg->pool_pages > INT32_MAX))
     return fail(KVQ_ERR_INVALID_ARG, "pool_pages must be in [1, 2^31 - 1] for a paged cache");
+  // Launch grids: the append kernels put the sequence in grid.z and the kv-head in
+  // grid.y, the combine kernel the sequence in grid.y (at most 65535 each); the
+  // decode kernel's 1-D grid holds (splits + window workgroups) per (sequence,
+  // kv-head), at most 2^31 - 1 workgroups.
+  if (cfg->batch > kvq::kMaxGridYZ || cfg->num_kv_heads > kvq::kMaxGridYZ)
+    return fail(KVQ_ERR_INVALID_ARG, "batch (%d) and num_kv_heads (%d) must be at most %d (launch grid limit)",
+                cfg->batch, cfg->num_kv_heads, kvq::kMaxGridYZ);
+  const Layout L = make_layout(cfg);
+  if (int64_t(L.B) * L.Hkv * (L.max_splits + L.win_blocks) > INT32_MAX)
+    return fail(KVQ_ERR_INVALID_ARG,
+                "batch * num_kv_heads * (%d splits + %d window workgroups) exceeds the 2^31 - 1 workgroups of "
+                "a launch", L.max_splits, L.win_blocks);
   return ok();
 }
 
@@ -155,6 +169,11 @@ struct kvq_cache {
   int32_t* table = nullptr;
   std::vector<int32_t> npages, owner;
   hipEvent_t table_done = nullptr;
+  // A launch of an append (or of the decode of a one-call step) failed: group
+  // blocks, window slots and device records may be partly written, so every
+  // sequence counts as undefined until kvq_reset_sequence has started it over.
+  bool broken = false;
+  std::vector<char> undefined;
 };
 
 extern "C" {
@@ -308,6 +327,22 @@ kvq_status kvq_set_profile_events(kvq_cache* c, hipEvent_t start, hipEvent_t sto
 
 namespace {
 
+// After a failed append launch every call that reads or extends the cache is
+// refused until each sequence has been reset.
+kvq_status refuse_if_broken(const kvq_cache* c) {
+  if (c->broken)
+    return fail(KVQ_ERR_HIP,
+                "an earlier append launch failed and left the cache contents undefined; reset every sequence "
+                "(kvq_reset_sequence) or destroy the cache");
+  return KVQ_OK;
+}
+
+kvq_status mark_broken(kvq_cache* c, kvq_status st) {
+  c->broken = true;
+  c->undefined.assign(c->cfg.batch, 1);
+  return st;
+}
+
 // An append that has been checked and described but not yet launched.
 struct PendingAppend {
   kvq::SeqArgs sa;
@@ -395,8 +430,10 @@ extern "C" {
 kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, const int32_t* n_tokens,
                       int32_t n_max, hipStream_t stream) {
   if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  if (refuse_if_broken(c) != KVQ_OK) return KVQ_ERR_HIP;
   PendingAppend pa;
   kvq_status st = prepare_append(c, k, v, n_tokens, n_max, stream, pa);
+  if (st == KVQ_ERR_HIP) return mark_broken(c, st);  // the record upload may have started
   if (st != KVQ_OK || pa.total_new == 0) return st;
   hipError_t e = hipSuccess;
   if (pa.max_flush > 0)
@@ -404,7 +441,7 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, const int32_t*
   // The window-write kernel always runs: with inline records it also stores them.
   if (e == hipSuccess && (pa.max_ring > 0 || pa.sa.inl_valid))
     e = kvq::launch_ring_write(c->L, c->base, pa.sa, k, v, n_max, std::max(pa.max_ring, 1), c->cfg.rotate, stream);
-  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append kernels failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return mark_broken(c, fail(KVQ_ERR_HIP, "append kernels failed: %s", hipGetErrorString(e)));
   c->T = pa.T2;
   c->Q = pa.Q2;
   return ok();
@@ -414,6 +451,7 @@ kvq_status kvq_decode_step(kvq_cache* c, const void* k, const void* v, const int
                            const void* q, float* out, hipStream_t stream) {
   if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
   if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q and out must be device pointers");
+  if (refuse_if_broken(c) != KVQ_OK) return KVQ_ERR_HIP;
   PendingAppend pa;
   // Checks that need no launch come first, so that a failing call changes nothing.
   {
@@ -425,6 +463,7 @@ kvq_status kvq_decode_step(kvq_cache* c, const void* k, const void* v, const int
     }
   }
   kvq_status st = prepare_append(c, k, v, n_tokens, n_max, stream, pa);
+  if (st == KVQ_ERR_HIP) return mark_broken(c, st);  // the record upload may have started
   if (st != KVQ_OK) return st;
   // Rotated caches keep the separate window-write kernel (it rotates the new keys);
   // otherwise the decode launch writes the new window tokens itself.
@@ -434,8 +473,11 @@ kvq_status kvq_decode_step(kvq_cache* c, const void* k, const void* v, const int
     e = kvq::launch_flush(c->L, c->base, pa.sa, k, v, n_max, pa.max_flush, c->cfg.rotate, stream);
   if (e == hipSuccess && pa.total_new > 0 && !fold && (pa.max_ring > 0 || pa.sa.inl_valid))
     e = kvq::launch_ring_write(c->L, c->base, pa.sa, k, v, n_max, std::max(pa.max_ring, 1), c->cfg.rotate, stream);
-  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append kernels failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return mark_broken(c, fail(KVQ_ERR_HIP, "append kernels failed: %s", hipGetErrorString(e)));
   st = launch_decode_for(c, pa.T2, pa.Q2, fold ? &pa : nullptr, k, v, n_max, q, out, stream);
+  // The decode launch may already have written the appended window tokens (and,
+  // with uploaded records, the device state) when it fails.
+  if (st == KVQ_ERR_HIP && pa.total_new > 0) return mark_broken(c, st);
   if (st != KVQ_OK) return st;
   c->T = pa.T2;
   c->Q = pa.Q2;
@@ -445,6 +487,7 @@ kvq_status kvq_decode_step(kvq_cache* c, const void* k, const void* v, const int
 kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, hipStream_t stream) {
   if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
   if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q and out must be device pointers");
+  if (refuse_if_broken(c) != KVQ_OK) return KVQ_ERR_HIP;
   return launch_decode_for(c, c->T, c->Q, nullptr, nullptr, nullptr, 0, q, out, stream);
 }
 
@@ -549,6 +592,10 @@ kvq_status kvq_reset_sequence(kvq_cache* c, int32_t b) {
   if (b < 0 || b >= c->cfg.batch) return fail(KVQ_ERR_INVALID_ARG, "sequence index %d out of range", b);
   c->T[b] = 0;
   c->Q[b] = 0;
+  if (c->broken) {
+    c->undefined[b] = 0;
+    c->broken = std::find(c->undefined.begin(), c->undefined.end(), 1) != c->undefined.end();
+  }
   if (c->L.P) {
     const int32_t* row = c->table + size_t(b) * c->L.max_pages;
     for (int32_t i = 0; i < c->npages[b]; i++) c->owner[row[i]] = -1;
@@ -587,9 +634,21 @@ kvq_status kvq_fp16_workspace_bytes(const kvq_fp16_config* cfg, size_t* bytes) {
   return ok();
 }
 
-kvq_status kvq_fp16_decode_attention(const kvq_fp16_config* cfg, const void* k, const void* v,
-                                     const int32_t* seq_lens, int64_t max_len, const void* q, float* out,
-                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checked FP16-decode launch shape: nsplit splits of cps 32-token chunks per
+// (sequence, kv-head); partials [B][Hq][nsplit][130] fp32.
+struct Fp16Plan {
+  int64_t nsplit = 0, cps = 0;
+  float scale_log2 = 0.0f;
+  size_t partial_bytes = 0;
+};
+
+// Host-side argument checks of an FP16-decode call.
+kvq_status check_fp16(const kvq_fp16_config* cfg, const void* k, const void* v, const int32_t* seq_lens,
+                      int64_t max_len, const void* q, const float* out) {
   if (!cfg) return fail(KVQ_ERR_INVALID_ARG, "cfg is NULL");
   const int ratio = cfg->num_kv_heads > 0 ? cfg->num_q_heads / cfg->num_kv_heads : 0;
   if (cfg->batch < 1 || cfg->num_kv_heads < 1 || cfg->num_q_heads % cfg->num_kv_heads != 0 ||
@@ -600,12 +659,15 @@ kvq_status kvq_fp16_decode_attention(const kvq_fp16_config* cfg, const void* k, 
     return fail(KVQ_ERR_INVALID_ARG, "t_cap must be in [1, 2^30]");
   if (max_len < 1 || max_len > cfg->t_cap)
     return fail(KVQ_ERR_INVALID_ARG, "max_len must be in [1, t_cap]");
-  if (!k || !v || !seq_lens || !q || !out || !workspace)
-    return fail(KVQ_ERR_INVALID_ARG, "k, v, seq_lens, q, out and workspace must be device pointers");
-  size_t need = 0;
-  kvq_status st = kvq_fp16_workspace_bytes(cfg, &need);
-  if (st != KVQ_OK) return st;
-  if (workspace_bytes < need) return fail(KVQ_ERR_OOM, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (cfg->batch > kvq::kMaxGridYZ)
+    return fail(KVQ_ERR_INVALID_ARG, "batch must be at most %d (launch grid limit)", kvq::kMaxGridYZ);
+  if (!k || !v || !seq_lens || !q || !out)
+    return fail(KVQ_ERR_INVALID_ARG, "k, v, seq_lens, q and out must be device pointers");
+  return ok();
+}
+
+// The split plan of a checked FP16-decode call (queries the current device).
+kvq_status plan_fp16(const kvq_fp16_config* cfg, int64_t max_len, Fp16Plan& p) {
   int ndev = 0, dev = 0, cus = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
     (void)hipGetLastError();
@@ -624,12 +686,42 @@ kvq_status kvq_fp16_decode_attention(const kvq_fp16_config* cfg, const void* k, 
     cps = (nch + kvq::kFp16MaxSplits - 1) / kvq::kFp16MaxSplits;
     nsplit = (nch + cps - 1) / cps;
   }
+  if (nsplit * bh > INT32_MAX) return fail(KVQ_ERR_INVALID_ARG, "too many workgroups for one launch");
   const float scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / std::sqrt(float(cfg->head_dim));
+  p.nsplit = nsplit;
+  p.cps = cps;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.partial_bytes = size_t(cfg->batch) * cfg->num_q_heads * size_t(nsplit) * kvq::kPartialStride * 4;
+  return ok();
+}
+
+kvq_status launch_fp16_plan(const kvq_fp16_config* cfg, const Fp16Plan& p, const void* k, const void* v,
+                            const int32_t* seq_lens, const void* q, float* out, float* part, hipStream_t stream) {
   const hipError_t e = kvq::launch_fp16_decode(k, v, seq_lens, cfg->t_cap, cfg->batch, cfg->num_q_heads,
-                                               cfg->num_kv_heads, scale * 1.4426950408889634f, q, out,
-                                               static_cast<float*>(workspace), int(nsplit), int(cps), stream);
+                                               cfg->num_kv_heads, p.scale_log2, q, out, part, int(p.nsplit),
+                                               int(p.cps), stream);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "fp16 decode launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_fp16_decode_attention(const kvq_fp16_config* cfg, const void* k, const void* v,
+                                     const int32_t* seq_lens, int64_t max_len, const void* q, float* out,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  kvq_status st = check_fp16(cfg, k, v, seq_lens, max_len, q, out);
+  if (st != KVQ_OK) return st;
+  if (!workspace) return fail(KVQ_ERR_INVALID_ARG, "workspace must be a device pointer");
+  size_t need = 0;
+  st = kvq_fp16_workspace_bytes(cfg, &need);
+  if (st != KVQ_OK) return st;
+  if (workspace_bytes < need) return fail(KVQ_ERR_OOM, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  Fp16Plan p;
+  st = plan_fp16(cfg, max_len, p);
+  if (st != KVQ_OK) return st;
+  return launch_fp16_plan(cfg, p, k, v, seq_lens, q, out, static_cast<float*>(workspace), stream);
 }
 
 }  // extern "C"

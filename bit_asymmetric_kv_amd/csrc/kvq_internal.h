@@ -13,6 +13,7 @@ constexpr int kMinGroupsPerSplit = 4;
 constexpr int kMaxSplits = 2048;
 constexpr int kMaxResidual = 4096;
 constexpr int kMaxPageGroups = 1 << 16;  // groups per page of a paged cache
+constexpr int kMaxGridYZ = 65535;        // launch grid limit in y and z
 // The FP16 window [o + Q, T) holds at most residual + group - 1 tokens: residual / 32
 // + 1 chunks of 32 tokens, plus one chunk for an attention sink; four chunks per
 // decode workgroup.

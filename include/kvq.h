@@ -38,8 +38,13 @@
  *  - Device pointers are plain device addresses (for example a torch tensor's
  *    data_ptr()); host pointers are ordinary host memory. Callers own every
  *    buffer they pass, and it must stay valid until the stream has passed the call.
- *  - All argument checks run on the host before any launch; on any error the cache
- *    state is unchanged and kvq_last_error() describes the problem.
+ *  - All argument checks run on the host before any launch; on any error they find
+ *    the cache state is unchanged and kvq_last_error() describes the problem.
+ *  - KVQ_ERR_HIP from kvq_append or kvq_decode_step means a HIP call or launch of
+ *    the append failed after work may have been enqueued: group blocks, FP16 window
+ *    slots and device records can be partly written. The cache then refuses
+ *    kvq_append, kvq_decode_step and kvq_decode_attention (KVQ_ERR_HIP) until every
+ *    sequence has been started over with kvq_reset_sequence, or it is destroyed.
  *  - Calls are asynchronous on `stream` unless stated. A handle is not thread safe.
  *  - Inputs holding NaN or Inf give undefined results (they are not scanned).
  */
@@ -67,9 +72,11 @@ typedef enum {
 } kvq_status;
 
 typedef struct {
-  int32_t batch;         /* B >= 1 sequences */
+  int32_t batch;         /* B: 1 .. 65535 sequences (launch grid limit) */
   int32_t num_q_heads;   /* Hq; a multiple of num_kv_heads */
-  int32_t num_kv_heads;  /* Hkv >= 1; Hq / Hkv must be 1, 2, 4 or 8 */
+  int32_t num_kv_heads;  /* Hkv: 1 .. 65535; Hq / Hkv must be 1, 2, 4 or 8. Also
+                            B * Hkv * (decode splits + window workgroups) must stay below
+                            2^31 (the decode launch's workgroups), checked at creation */
   int32_t head_dim;      /* D; must be 128 */
   int32_t bits;          /* 2, 3 or 4 */
   int32_t group;         /* G: tokens per key group = channels per value group; must be 32 */
@@ -166,7 +173,9 @@ void kvq_destroy(kvq_cache* c);
 kvq_status kvq_set_pages(kvq_cache* c, int32_t b, const int32_t* pages, int32_t n, hipStream_t stream);
 
 /* Start sequence b over (T = Q = 0); in a paged cache its pages become free.
- * Host-side only: the next append rewrites what the kernels read. */
+ * Host-side only: the next append rewrites what the kernels read. After a failed
+ * append launch (KVQ_ERR_HIP) the cache is usable again once every sequence has
+ * been reset this way. */
 kvq_status kvq_reset_sequence(kvq_cache* c, int32_t b);
 
 /* Host mirror of sequence b: T = tokens appended, Q = tokens held quantized

@@ -54,6 +54,25 @@ def test_invalid_configs_rejected_before_any_device_call(field, value):
     assert msg
 
 
+@pytest.mark.parametrize("batch,hq,hkv,max_tokens", [
+    (65536, 8, 8, 1000),            # sequences in grid.z / grid.y of the append and combine launches
+    (1, 65536, 65536, 1000),        # kv-heads in grid.y of the append launches
+    (65535, 32, 32, 1 << 20),       # 2.1e6 (sequence, kv-head) pairs x 2049 decode workgroups overflow the 1-D grid
+    (40000, 8 * 60000, 60000, 64),  # within the per-axis limits, but 2.4e9 (sequence, kv-head) pairs
+])
+def test_launch_grid_limits_rejected_before_any_device_call(batch, hq, hkv, max_tokens):
+    cfg = kvq.make_config(batch, hq, hkv, residual=32, max_tokens=max_tokens)
+    s, msg = _status(cfg)
+    assert s == _lib.KVQ_ERR_INVALID_ARG, (batch, hkv, s, msg)
+    assert "grid" in msg or "workgroups" in msg
+
+
+def test_largest_grid_shapes_pass_validation():
+    # at the limits the configuration is valid (only its size is asked for: no device call)
+    assert kvq.cache_bytes(kvq.make_config(65535, 8, 8, residual=0, max_tokens=32)) > 0
+    assert kvq.cache_bytes(kvq.make_config(1, 65535, 65535, residual=0, max_tokens=32)) > 0
+
+
 def test_paged_cache_needs_a_pool():
     cfg = kvq.make_config(1, 8, 8, residual=32, max_tokens=100, page_groups=4, pool_pages=0)
     assert _status(cfg)[0] == _lib.KVQ_ERR_INVALID_ARG
