@@ -80,9 +80,12 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_asymmetric_kv_amd.build_lib`")
-    lib = ctypes.CDLL(LIB_PATH)
+    # KVQ_LIBRARY names another build of the same library (the host-sanitizer build
+    # that the CPU tests load in a child process)
+    path = os.environ.get("KVQ_LIBRARY", LIB_PATH)
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m bit_asymmetric_kv_amd.build_lib`")
+    lib = ctypes.CDLL(path)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     cfgp = ctypes.POINTER(KVQConfig)
     lib.kvq_cache_bytes.argtypes = [cfgp, ctypes.POINTER(sz)]
@@ -326,6 +329,9 @@ class Fp16Decode:
                 raise ValueError(f"{name} must be a contiguous {dt} device tensor of shape {shape}")
         if out is None:
             out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=torch.float32, device=self.device)
+        elif (out.dtype != torch.float32 or tuple(out.shape) != (c.batch, c.num_q_heads, c.head_dim)
+              or not out.is_contiguous() or not out.is_cuda):
+            raise ValueError("out must be a contiguous float32 device tensor of shape [B, Hq, D]")
         check(load().kvq_fp16_decode_attention(
             ctypes.byref(c), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
             ctypes.c_void_p(seq_lens.data_ptr()), int(max_len), ctypes.c_void_p(q.data_ptr()),
