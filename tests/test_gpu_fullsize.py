@@ -46,7 +46,9 @@ def _check_blocks(cache, oh, b, h, group_sample):
         assert np.array_equal(rv[slot].view(np.uint16), oh.v16[t].view(np.uint16)), f"ring value t={t}"
 
 
-def _run_full(w, dev, sample, steps, check_steps, group_sample=lambda ng: range(ng)):
+def _run_full(w, dev, sample, steps, check_steps, group_sample=lambda ng: range(ng), one_call=False):
+    """one_call: each step is one kvq_decode_step (append + decode in one call, the
+    window write folded into the decode launch), as the bench times it."""
     import bit_asymmetric_kv_amd as kvq
     lens = w.context_lengths()
     max_tokens = int(lens.max()) + steps + 1
@@ -58,7 +60,8 @@ def _run_full(w, dev, sample, steps, check_steps, group_sample=lambda ng: range(
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 101 + 7)
     print(f"case full-size {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} bits={w.bits} "
-          f"R={w.residual} rot={w.rotate} context max {int(lens.max())} steps={steps} sample={sample}", flush=True)
+          f"R={w.residual} rot={w.rotate} context max {int(lens.max())} steps={steps} sample={sample} "
+          f"one_call={one_call}", flush=True)
     done = np.zeros(w.batch, dtype=np.int64)
     while np.any(done < lens):
         n = np.minimum(lens - done, CHUNK)
@@ -74,11 +77,14 @@ def _run_full(w, dev, sample, steps, check_steps, group_sample=lambda ng: range(
     worst = 0.0
     for s in range(steps):
         k, v = wl.torch_kv(torch, w, params, 1, gen, dev)
-        cache.append(k, v)
         for (b, h), oh in oracles.items():
             oh.append(k[b, :1, h].cpu().numpy(), v[b, :1, h].cpu().numpy())
         q = torch.randn((w.batch, w.num_q_heads, w.head_dim), generator=gen, device=dev).to(torch.float16)
-        out = cache.decode(q)
+        if one_call:
+            out = cache.step(k, v, q)
+        else:
+            cache.append(k, v)
+            out = cache.decode(q)
         if s in check_steps:
             torch.cuda.synchronize()
             got = out.cpu().numpy().astype(np.float64)
@@ -107,6 +113,17 @@ def test_full_llama2_7b_b8_32k(dev):
 @pytest.mark.parametrize("name", ["gqa_128k_2bit", "gqa_128k_3bit", "gqa_128k_4bit"])
 def test_full_gqa_128k(dev, name):
     _run_full(wl.WORKLOADS[name], dev, [(0, 0), (0, 5)], 1, {0})
+
+
+def test_full_gqa_128k_one_call_steps(dev):
+    # the bench's step: kvq_decode_step with the automatic (weighted) split plan over
+    # 40 steps, so one group leaves the window (T - R crosses 131072 + 32 at step 31)
+    _run_full(wl.WORKLOADS["gqa_128k_2bit"], dev, [(0, 0), (0, 3), (0, 6)], 40, {0, 30, 31, 39}, one_call=True)
+
+
+def test_full_llama2_7b_b8_32k_one_call_steps(dev):
+    # batch 8: the folded window write with inline sequence records, flush at step 31
+    _run_full(wl.WORKLOADS["llama2_7b_b8_32k"], dev, [(0, 0), (5, 20)], 33, {0, 31, 32}, one_call=True)
 
 
 def test_full_gqa_128k_hg8(dev):
