@@ -31,7 +31,7 @@ EXPORTED = (
     "kvq_cache_bytes", "kvq_create", "kvq_append", "kvq_decode_attention", "kvq_set_decode_split",
     "kvq_destroy", "kvq_seq_len", "kvq_group_bytes", "kvq_read_state", "kvq_last_error",
     "kvq_set_profile_events", "kvq_decode_step", "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention",
-    "kvq_set_pages", "kvq_reset_sequence",
+    "kvq_set_pages", "kvq_reset_sequence", "kvq_fp16_decode_attention_noalloc",
 )
 
 
@@ -107,12 +107,13 @@ def load() -> ctypes.CDLL:
     lib.kvq_stream_read.argtypes = [vp, sz, vp, vp]
     lib.kvq_fp16_workspace_bytes.argtypes = [f16p, ctypes.POINTER(sz)]
     lib.kvq_fp16_decode_attention.argtypes = [f16p, vp, vp, vp, i64, vp, vp, vp, sz, vp]
+    lib.kvq_fp16_decode_attention_noalloc.argtypes = [f16p, vp, vp, vp, i64, vp, vp, vp]
     lib.kvq_set_pages.argtypes = [vp, i32, ctypes.POINTER(i32), i32, vp]
     lib.kvq_reset_sequence.argtypes = [vp, i32]
     for name in ("kvq_cache_bytes", "kvq_create", "kvq_append", "kvq_decode_attention",
                  "kvq_set_decode_split", "kvq_seq_len", "kvq_read_state", "kvq_set_profile_events",
                  "kvq_decode_step", "kvq_stream_read", "kvq_fp16_workspace_bytes", "kvq_fp16_decode_attention",
-                 "kvq_set_pages", "kvq_reset_sequence"):
+                 "kvq_set_pages", "kvq_reset_sequence", "kvq_fp16_decode_attention_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -308,14 +309,20 @@ class Fp16Decode:
     """Decode attention over a plain FP16 cache k, v [B, Hkv, t_cap, D] (comparison
     baseline of the quantized path). Owns its workspace as a torch tensor."""
 
-    def __init__(self, batch, num_q_heads, num_kv_heads, t_cap, head_dim=128, softmax_scale=0.0, device="cuda"):
+    def __init__(self, batch, num_q_heads, num_kv_heads, t_cap, head_dim=128, softmax_scale=0.0, device="cuda",
+                 static_scratch=False):
+        """static_scratch: call kvq_fp16_decode_attention_noalloc, whose split partials
+        live in the library's static per-GPU scratch (no workspace is allocated)."""
         import torch
         self._torch = torch
         self.device = torch.device(device)
         self.cfg = KVQFp16Config(batch, num_q_heads, num_kv_heads, head_dim, t_cap, softmax_scale)
-        nbytes = ctypes.c_size_t(0)
-        check(load().kvq_fp16_workspace_bytes(ctypes.byref(self.cfg), ctypes.byref(nbytes)))
-        self.workspace = torch.empty(nbytes.value, dtype=torch.uint8, device=self.device)
+        self.static_scratch = bool(static_scratch)
+        self.workspace = None
+        if not self.static_scratch:
+            nbytes = ctypes.c_size_t(0)
+            check(load().kvq_fp16_workspace_bytes(ctypes.byref(self.cfg), ctypes.byref(nbytes)))
+            self.workspace = torch.empty(nbytes.value, dtype=torch.uint8, device=self.device)
 
     def __call__(self, k, v, seq_lens, max_len, q, out=None):
         """k, v: fp16 [B, Hkv, t_cap, D]; seq_lens: int32 [B] on the device; q: fp16 [B, Hq, D]."""
@@ -332,9 +339,16 @@ class Fp16Decode:
         elif (out.dtype != torch.float32 or tuple(out.shape) != (c.batch, c.num_q_heads, c.head_dim)
               or not out.is_contiguous() or not out.is_cuda):
             raise ValueError("out must be a contiguous float32 device tensor of shape [B, Hq, D]")
-        check(load().kvq_fp16_decode_attention(
-            ctypes.byref(c), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-            ctypes.c_void_p(seq_lens.data_ptr()), int(max_len), ctypes.c_void_p(q.data_ptr()),
-            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(self.workspace.data_ptr()),
-            self.workspace.numel(), ctypes.c_void_p(_stream_ptr(torch, self.device))))
+        stream = ctypes.c_void_p(_stream_ptr(torch, self.device))
+        if self.static_scratch:
+            check(load().kvq_fp16_decode_attention_noalloc(
+                ctypes.byref(c), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                ctypes.c_void_p(seq_lens.data_ptr()), int(max_len), ctypes.c_void_p(q.data_ptr()),
+                ctypes.c_void_p(out.data_ptr()), stream))
+        else:
+            check(load().kvq_fp16_decode_attention(
+                ctypes.byref(c), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                ctypes.c_void_p(seq_lens.data_ptr()), int(max_len), ctypes.c_void_p(q.data_ptr()),
+                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(self.workspace.data_ptr()),
+                self.workspace.numel(), stream))
         return out

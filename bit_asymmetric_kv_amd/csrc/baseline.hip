@@ -9,7 +9,14 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kvq_internal.h"
+
+// Split partials of the FP16-cache decode for callers that cannot allocate: one
+// copy per GPU, held until the process ends. In host code this name is only a
+// stand-in for the symbol; its device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[kvq::kFp16ScratchBytes];
 
 namespace kvq {
 namespace {
@@ -187,6 +194,26 @@ hipError_t launch_fp16(const Fp16Args& a, int B, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t fp16_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // first use on this device (the current one): its own copy of the array
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* fold, int blocks, hipStream_t stream) {
   hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const u32x4*>(buf),

@@ -724,6 +724,25 @@ kvq_status kvq_fp16_decode_attention(const kvq_fp16_config* cfg, const void* k, 
   return launch_fp16_plan(cfg, p, k, v, seq_lens, q, out, static_cast<float*>(workspace), stream);
 }
 
+kvq_status kvq_fp16_decode_attention_noalloc(const kvq_fp16_config* cfg, const void* k, const void* v,
+                                             const int32_t* seq_lens, int64_t max_len, const void* q, float* out,
+                                             hipStream_t stream) {
+  kvq_status st = check_fp16(cfg, k, v, seq_lens, max_len, q, out);
+  if (st != KVQ_OK) return st;
+  Fp16Plan p;
+  st = plan_fp16(cfg, max_len, p);
+  if (st != KVQ_OK) return st;
+  if (p.partial_bytes > kvq::kFp16ScratchBytes)
+    return fail(KVQ_ERR_CAPACITY,
+                "this shape needs %zu bytes of split partials; the static scratch holds %zu (use "
+                "kvq_fp16_decode_attention with a workspace)",
+                p.partial_bytes, kvq::kFp16ScratchBytes);
+  void* part = nullptr;
+  const hipError_t e = kvq::fp16_scratch(&part);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "looking up the static scratch failed: %s", hipGetErrorString(e));
+  return launch_fp16_plan(cfg, p, k, v, seq_lens, q, out, static_cast<float*>(part), stream);
+}
+
 }  // extern "C"
 
 namespace {

@@ -158,5 +158,10 @@ hipError_t launch_fp16_decode(const void* k, const void* v, const int32_t* lens,
                               int Hkv, float scale_log2, const void* q, float* out, float* part, int nsplit,
                               int cps, hipStream_t stream);
 constexpr int kFp16MaxSplits = 1024;
+// The FP16-cache decode's static scratch (partials of the variant that allocates
+// nothing): 4 MiB per GPU, room for 8065 partials of 520 bytes.
+constexpr size_t kFp16ScratchBytes = size_t(4) << 20;
+// Device address of that scratch on the current device (looked up once per device).
+hipError_t fp16_scratch(void** ptr);
 
 }  // namespace kvq

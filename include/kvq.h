@@ -256,6 +256,21 @@ kvq_status kvq_fp16_decode_attention(const kvq_fp16_config* cfg, const void* k, 
                                      const int32_t* seq_lens, int64_t max_len, const void* q, float* out,
                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* kvq_fp16_decode_attention without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments (less the workspace), checks, split plan and
+ * results as kvq_fp16_decode_attention; the split partials go to a static scratch
+ * array of 4 MiB that the library holds on each GPU it runs on until the process
+ * ends (its address is looked up once per device, on the first call there). The
+ * call allocates nothing. Shapes whose partials, B * Hq * splits * 520 bytes, exceed
+ * 4 MiB are refused with KVQ_ERR_CAPACITY. Every call on one GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (other streams, other threads) race and
+ * must be ordered by the caller. Nothing in the scratch needs to start at zero:
+ * every partial a call reads is written by the same call. */
+kvq_status kvq_fp16_decode_attention_noalloc(const kvq_fp16_config* cfg, const void* k, const void* v,
+                                             const int32_t* seq_lens, int64_t max_len, const void* q, float* out,
+                                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
