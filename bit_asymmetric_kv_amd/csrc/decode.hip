@@ -511,7 +511,10 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
     }
   }
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const SeqDesc sd = (a.app.pending && a.app.seq.inl_valid) ? a.app.seq.inl[b] : a.seq[b];
+  // Small batches pass every sequence's record in the arguments (the host mirror of
+  // the lengths this launch sees), so no workgroup waits on a record load before
+  // its first group loads go out.
+  const SeqDesc sd = a.app.seq.inl_valid ? a.app.seq.inl[b] : a.seq[b];
   const int T = sd.t_old + sd.n_new, Q = sd.q_new;
   const int ng = Q / kG;
 
@@ -530,17 +533,17 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
     g1 = split == nsb - 1 ? ng : bound(split + 1);
   }
   const int len = tail ? 0 : max(0, g1 - g0);
-  const int per = (len + kWaves - 1) / kWaves;
-  // wave-uniform (kept in scalar registers: a paged cache's table entries are then
-  // scalar loads)
-  const int wg0 = __builtin_amdgcn_readfirstlane(g0 + wave * per);
-  const int wg1 = min(g1, wg0 + per);
-  // Wave-uniform (the wave index is), so the loop's waits branch on scalars.
-  const int n = __builtin_amdgcn_readfirstlane(tail ? 0 : max(0, wg1 - wg0));
+  // The waves take the split's groups in turn (wave w: groups g0 + w, g0 + w + 4,
+  // ...), so their counts differ by at most one and they reach the partial merge
+  // together. Wave-uniform (kept in scalar registers: a paged cache's table entries
+  // are then scalar loads, and the loop's waits branch on scalars).
+  const int wg0 = __builtin_amdgcn_readfirstlane(g0 + wave);
+  const int n = __builtin_amdgcn_readfirstlane(max(0, (len - wave + kWaves - 1) / kWaves));
+  auto group_of = [&](int r) { return wg0 + kWaves * r; };  // r-th group of this wave
 
   // Group r's bytes of this lane, loaded straight into registers.
   auto load_group = [&](int r, GroupRegs<BITS, NJ>& G) {
-    const uint8_t* blk = a.store.at(b, h, wg0 + r);
+    const uint8_t* blk = a.store.at(b, h, group_of(r));
     constexpr int CB = kG * kD * BITS / 8;
     G.kc0 = *reinterpret_cast<const uint4*>(blk + 16 * lane);
     G.vc0 = *reinterpret_cast<const uint4*>(blk + CB + 16 * lane);
@@ -557,7 +560,7 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
       // lanes 0-31: the key scale / zero-point region; lanes 32-63: the rotary
       // cos / sin of the group's start position
       G.ks = lane < 32 ? load_half8(blk + 2 * CB + 16 * lane)
-                       : load_half8(reinterpret_cast<const uint8_t*>(a.rope_tab + size_t(wg0 + r) * kD) +
+                       : load_half8(reinterpret_cast<const uint8_t*>(a.rope_tab + size_t(group_of(r)) * kD) +
                                     16 * (lane - 32));
     } else {
       G.ks = load_half8(blk + 2 * CB + 16 * (lane / 4));

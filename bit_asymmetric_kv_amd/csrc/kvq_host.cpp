@@ -823,6 +823,11 @@ kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const 
     app.v = v;
     app.n_max = n_max;
     app.seq = pa->sa;
+  } else if (B <= kvq::kInlineSeqs) {
+    // no append in this launch: the records the kernels read are the host mirror's
+    for (int b = 0; b < B; b++)
+      app.seq.inl[b] = SeqDesc{int32_t(T[b]), 0, int32_t(Q[b]), int32_t(Q[b])};
+    app.seq.inl_valid = 1;
   }
   hipError_t e = kvq::launch_decode(c->L, c->base, dev_seq, app, q, out, int32_t(gps), plan,
                                     scale_log2, c->cfg.rotate, stream, c->prof_start, c->prof_stop);
