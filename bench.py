@@ -14,10 +14,18 @@ stepped round-robin so that consecutive steps never find their cache in the
 Prints one JSON line. `value` is the effective bandwidth of a whole step:
 algorithmic bytes (packed codes + fp16 scales/zero-points + fp16 window) divided
 by the step time, measured over the timed steps with one pair of HIP events
-bracketing them (no per-step records: each event record costs microseconds of
-GPU time here). `roofline` reports the dominant kernel (the decode split kernel),
-timed in a second pass of decode calls on the same caches with HIP events that the
-library records around that kernel on its own stream.
+bracketing them (no per-step records). `roofline` reports the dominant kernel (the
+decode split kernel), timed in a second pass of decode calls on the same caches
+with HIP events that the library records around that kernel on its own stream.
+Every event is created without the system-scope fence (hipEventDisableSystemFence):
+a default event record writes back and invalidates the caches, which costs several
+microseconds per record and lengthens the kernel it brackets.
+
+Steady state: cache c is prefilled with a few extra tokens (under 32) so that, when
+the timed steps start, it sits 31 - 32 c / copies appends past its last group flush;
+the timed steps then contain about steps / 32 group flushes, spread over the caches,
+whatever the number of steps. A separate pass times single steps and reports the
+steps with a group flush apart from the others.
 """
 from __future__ import annotations
 
@@ -36,6 +44,7 @@ sys.path.insert(0, ROOT)
 import kvq_workloads as wl  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+EVENT_NO_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
 
 class HipEvents:
@@ -43,7 +52,7 @@ class HipEvents:
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
@@ -53,8 +62,8 @@ class HipEvents:
         out = []
         for _ in range(n):
             e = ctypes.c_void_p(0)
-            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), EVENT_NO_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(e.value)
         return out
 
@@ -76,17 +85,40 @@ class HipEvents:
 PREFILL_CHUNK = 131072
 
 
-def build_caches(torch, kvq, w, copies, max_tokens, dev, gps, ev=None, stream=None, page_groups=0):
+def steady_offsets(w, copies, warmup):
+    """Extra prefill tokens per cache copy (0..31): copy c then starts the timed steps
+    31 - 32 c / copies appends past its last group flush, judged on sequence 0 (all
+    sequences of an equal-length workload share it; ragged ones have their own)."""
+    o = 1 if w.sink else 0
+    T0 = int(w.context_lengths()[0])
+    out = []
+    for c in range(copies):
+        appends = len(range(c, warmup, copies))   # warmup steps that reach copy c
+        phase = 31 - (32 * c) // copies
+        out.append((phase - (T0 + appends - o - w.residual)) % 32)
+    return out
+
+
+def will_flush(T, w):
+    """Whether appending one token to a sequence holding T tokens moves a group out
+    of its FP16 window (the residual rule, as the library applies it)."""
+    o = 1 if w.sink else 0
+    q = lambda t: 32 * (max(0, t - o - w.residual) // 32)
+    return q(T + 1) != q(T)
+
+
+def build_caches(torch, kvq, w, copies, max_tokens, dev, gps, ev=None, stream=None, page_groups=0, extra=None):
     """Build `copies` caches holding the workload's prefill (appends of up to
-    PREFILL_CHUNK tokens per sequence: one append for contexts up to 128K).
+    PREFILL_CHUNK tokens per sequence: one append for contexts up to 128K), copy c
+    with extra[c] more tokens per sequence if given.
     With `ev`, each copy's appends are timed (inputs drawn beforehand) and the
     per-copy prefill times in ms are returned as well. With `page_groups`, each cache
     is paged and every sequence gets its pages in a seeded random order."""
     params = wl.torch_key_params(torch, w, dev)
     caches, times = [], []
-    lens = w.context_lengths()
     chunk = PREFILL_CHUNK
     for c in range(copies):
+        lens = w.context_lengths() + (extra[c] if extra else 0)
         paged = {}
         if page_groups:
             max_pages = -(-((max_tokens + w.group - 1) // w.group) // page_groups)
@@ -136,53 +168,103 @@ def step_bytes(cache, w):
     return total
 
 
-def cpu_baseline(w, heads=4, steps=20):
-    """Time the CPU oracle (single BLAS thread) on `heads` KV heads of sequence 0 at
-    the workload's full context: per step, append one token and attend."""
-    from threadpoolctl import threadpool_limits
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, heads=2, steps=4):
+    """Time the CPU oracle on `heads` KV heads of sequence 0 at the workload's full
+    context, twice: with numpy / BLAS at their default thread count and pinned to one
+    thread. Per run: the prefill (quantize the whole prompt), then `steps` steps of
+    append-1 + attend. The throughput `value` is the algorithmic bytes of the attended
+    steps over their time at the default thread count."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import OracleHead
     ratio = w.num_q_heads // w.num_kv_heads
     T0 = int(w.context_lengths()[0])
-    with threadpool_limits(1):
+    inputs = [(wl.keys(w, 0, h, 0, T0 + steps), wl.values(w, 0, h, 0, T0 + steps)) for h in range(heads)]
+    qs = [wl.queries(w, s)[0] for s in range(steps)]
+
+    def run():
+        t0 = time.perf_counter()
         hs = []
         for h in range(heads):
             oh = OracleHead(w.bits, w.residual, w.rotate, sink=w.sink, rope=w.rope)
-            oh.append(wl.keys(w, 0, h, 0, T0), wl.values(w, 0, h, 0, T0))
+            oh.append(inputs[h][0][:T0], inputs[h][1][:T0])
             hs.append(oh)
+        t1 = time.perf_counter()
         nbytes = 0
-        t0 = time.perf_counter()
         for s in range(steps):
-            q = wl.queries(w, s)[0]
             for h, oh in enumerate(hs):
-                oh.append(wl.keys(w, 0, h, oh.T, oh.T + 1), wl.values(w, 0, h, oh.T, oh.T + 1))
-                oh.attend(q[h * ratio:(h + 1) * ratio])
+                oh.append(inputs[h][0][oh.T:oh.T + 1], inputs[h][1][oh.T:oh.T + 1])
+                oh.attend(qs[s][h * ratio:(h + 1) * ratio])
                 nbytes += wl.algorithmic_bytes(oh.T, oh.Q, w.bits, w.group, w.head_dim)
-        dt = time.perf_counter() - t0
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"sequence 0, kv-heads 0..{heads - 1} (each with its {ratio} query heads) of "
-                      f"{w.name} at full context {T0}, {steps} steps of append-1 + attend; "
-                      f"{dt:.1f} s timed, numpy with one BLAS thread"}
+        t2 = time.perf_counter()
+        return {"prefill_s_per_head": round((t1 - t0) / heads, 3),
+                "step_s_per_head": round((t2 - t1) / (steps * heads), 3),
+                "total_s": round(t2 - t0, 2), "gbps": nbytes / (t2 - t1) / 1e9}
+
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    default = run()
+    with threadpool_limits(1):
+        single = run()
+    return {"value": default["gbps"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"sequence 0, kv-heads 0..{heads - 1} (each with its {ratio} query heads) of {w.name} at "
+                      f"full context {T0}: prefill, then {steps} steps of append-1 + attend, run once with "
+                      f"numpy/BLAS at {threads} threads and once at 1 thread",
+            "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+            "default_threads": default, "one_thread": single}
 
 
-def measure_comparisons(torch, kvq, w, ev, stream, dev, iters=20):
-    """Achievable HBM read bandwidth (streaming-read probe over 2 GiB) and the FP16-
-    cache decode on the workload's shapes (same tokens per sequence, two caches
-    round-robin), each timed with one pair of HIP events around `iters` calls."""
-    res = {}
-    buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
-    buf.fill_(1)
-    fold = torch.zeros(1, dtype=torch.int32, device=dev)
-    for _ in range(2):
-        kvq.stream_read(buf, fold)
-    torch.cuda.synchronize()
+def time_calls(ev, stream, torch, fn, iters):
+    """Average µs of `iters` calls of fn(i), bracketed by one pair of events."""
     a, b = ev.create(1)[0], ev.create(1)[0]
+    torch.cuda.synchronize()
     ev.record(a, stream)
-    for _ in range(iters):
-        kvq.stream_read(buf, fold)
+    for i in range(iters):
+        fn(i)
     ev.record(b, stream)
     torch.cuda.synchronize()
-    res["hbm_stream_read_gbps"] = round(buf.numel() * iters / (ev.elapsed_ms(a, b) * 1e-3) / 1e9, 1)
+    us = ev.elapsed_ms(a, b) / iters * 1e3
+    ev.destroy([a, b])
+    return us
+
+
+def measure_comparisons(torch, kvq, w, ev, stream, dev, nbytes, iters=20):
+    """Achievable HBM read bandwidth (streaming-read probe: over 2 GiB, and over
+    buffers of the decode's own byte count, round-robin so that none is cache
+    resident) and the FP16-cache decode on the workload's shapes (same tokens per
+    sequence, two caches round-robin), each timed with one pair of HIP events around
+    `iters` calls."""
+    res = {}
+    # two workgroups of 256 threads per compute unit: the fastest grid in a sweep of
+    # 1 to 64 per unit (101 MB to 2 GiB)
+    fold = torch.zeros(2 * torch.cuda.get_device_properties(dev).multi_processor_count, dtype=torch.int32,
+                       device=dev)
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    for _ in range(2):
+        kvq.stream_read(buf, fold)
+    us = time_calls(ev, stream, torch, lambda i: kvq.stream_read(buf, fold), iters)
+    res["hbm_stream_read_gbps"] = round(buf.numel() / (us * 1e-6) / 1e9, 1)
     del buf
+    nb = (int(nbytes) + 15) // 16 * 16
+    copies = max(2, min(8, (1 << 30) // nb))
+    bufs = [torch.ones(nb, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    for b_ in bufs:
+        kvq.stream_read(b_, fold)
+    us = time_calls(ev, stream, torch, lambda i: kvq.stream_read(bufs[i % copies], fold), 4 * iters)
+    res["stream_read_same_bytes_us"] = round(us, 2)
+    res["stream_read_same_bytes_gbps"] = round(nb / (us * 1e-6) / 1e9, 1)
+    del bufs
+    torch.cuda.empty_cache()
 
     lens = w.context_lengths() + 1
     t_cap = int(lens.max())
@@ -200,18 +282,11 @@ def measure_comparisons(torch, kvq, w, ev, stream, dev, iters=20):
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     for i in range(4):
         op(*caches[i % 2], lens_dev, t_cap, q, out)
-    torch.cuda.synchronize()
-    ev.record(a, stream)
-    for i in range(iters):
-        op(*caches[i % 2], lens_dev, t_cap, q, out)
-    ev.record(b, stream)
-    torch.cuda.synchronize()
-    us = ev.elapsed_ms(a, b) / iters * 1e3
+    us = time_calls(ev, stream, torch, lambda i: op(*caches[i % 2], lens_dev, t_cap, q, out), iters)
     fp16_bytes = int(lens.sum()) * w.num_kv_heads * 2 * 2 * w.head_dim
-    res.update({"fp16_decode_us": round(us, 2), "fp16_cache_bytes": fp16_bytes,
+    res.update({"fp16_decode_call_us": round(us, 2), "fp16_cache_bytes": fp16_bytes,
                 "fp16_decode_gbps": round(fp16_bytes / (us * 1e-6) / 1e9, 1),
                 "fp16_outputs_finite": bool(torch.isfinite(out).all())})
-    ev.destroy([a, b])
     del caches
     torch.cuda.synchronize()
     return res
@@ -282,8 +357,6 @@ def main():
         return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # 256 steps over 8 caches: each cache takes 32 appends, so every cache moves one
-    # group out of its FP16 window (one flush) inside the timed region, as in steady state.
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--kernel-iters", type=int, default=200,
@@ -293,6 +366,8 @@ def main():
     ap.add_argument("--groups-per-split", type=int, default=0)
     ap.add_argument("--page-groups", type=int, default=0,
                     help="paged caches with this many groups per page (pages in random order)")
+    ap.add_argument("--flush-split-steps", type=int, default=96,
+                    help="single steps timed one by one, steps with a group flush reported apart (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparisons", action="store_true",
                     help="skip the streaming-read probe and the FP16-cache decode")
@@ -312,91 +387,137 @@ def main():
     kvq.load()
     dev = torch.device("cuda:0")
     w = wl.WORKLOADS[args.workload]
-    total_steps = args.warmup + args.steps
-    max_tokens = int(w.context_lengths().max()) + total_steps + 64 + 1
-    print(f"[bench] building {args.copies} caches of {w.name}", file=sys.stderr, flush=True)
+    copies = args.copies
+    extra = steady_offsets(w, copies, args.warmup)
+    n_split = max(0, args.flush_split_steps)
+    n2 = min(args.steps, 64)
+    total_steps = args.warmup + args.steps + n_split + n2
+    max_tokens = int(w.context_lengths().max()) + 32 + total_steps + 1
+    print(f"[bench] building {copies} caches of {w.name}", file=sys.stderr, flush=True)
     ev = HipEvents()
     stream = torch.cuda.current_stream(dev).cuda_stream
-    caches, params, prefill_ms = build_caches(torch, kvq, w, args.copies, max_tokens, dev, args.groups_per_split,
-                                              ev, stream, args.page_groups)
+    caches, params, prefill_ms = build_caches(torch, kvq, w, copies, max_tokens, dev, args.groups_per_split,
+                                              ev, stream, args.page_groups, extra)
     # Prefill-side quantization throughput: every copy's prefill appends, timed.
-    lens = w.context_lengths()
-    pf_tokens = int(lens.sum())
+    lens0 = w.context_lengths()
+    rates = []
+    for c in range(copies):
+        lens_c = lens0 + extra[c]
+        out_b = sum(wl.algorithmic_bytes(int(t), 32 * (max(0, int(t) - (1 if w.sink else 0) - w.residual) // 32),
+                                         w.bits, w.group, w.head_dim) for t in lens_c) * w.num_kv_heads
+        rates.append((int(lens_c.sum()), out_b, prefill_ms[c]))
+    sel = rates[1:] if copies > 1 else rates   # the first copy's appends also warm the kernels up
+    pf_tokens, pf_out, pf_ms = sorted(sel, key=lambda r: r[2])[len(sel) // 2]
     pf_in_bytes = pf_tokens * w.num_kv_heads * 2 * 2 * w.head_dim
-    pf_out_per_head = sum(wl.algorithmic_bytes(int(t), int(q), w.bits, w.group, w.head_dim)
-                    for t, q in ((t, caches[0].seq_len(b)[1]) for b, t in enumerate(lens)))
-    pf_med = float(np.median(prefill_ms[1:] if len(prefill_ms) > 1 else prefill_ms))
-    prefill = {"tokens_per_sequence_max": int(lens.max()), "kv_heads": w.num_kv_heads,
-               "us": round(pf_med * 1e3, 1),
-               "tokens_per_s": round(pf_tokens / (pf_med * 1e-3), 1),
-               "input_fp16_gbps": round(pf_in_bytes / (pf_med * 1e-3) / 1e9, 1),
-               "in_plus_out_gbps": round((pf_in_bytes + pf_out_per_head * w.num_kv_heads) / (pf_med * 1e-3) / 1e9, 1),
+    prefill = {"tokens_per_sequence_max": int(lens0.max()), "kv_heads": w.num_kv_heads,
+               "us": round(pf_ms * 1e3, 1),
+               "tokens_per_s": round(pf_tokens / (pf_ms * 1e-3), 1),
+               "input_fp16_gbps": round(pf_in_bytes / (pf_ms * 1e-3) / 1e9, 1),
+               "in_plus_out_gbps": round((pf_in_bytes + pf_out) / (pf_ms * 1e-3) / 1e9, 1),
                "append_tokens_max": PREFILL_CHUNK, "copies_timed": len(prefill_ms)}
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 7919)
-    knew, vnew = wl.torch_kv(torch, w, params, total_steps + 64, gen, dev)   # [B, steps, Hkv, D]
-    knew = knew.transpose(0, 1).contiguous().view(total_steps + 64, w.batch, 1, w.num_kv_heads, w.head_dim)
-    vnew = vnew.transpose(0, 1).contiguous().view(total_steps + 64, w.batch, 1, w.num_kv_heads, w.head_dim)
-    knew2, vnew2 = knew[total_steps:], vnew[total_steps:]
+    knew, vnew = wl.torch_kv(torch, w, params, total_steps, gen, dev)   # [B, steps, Hkv, D]
+    knew = knew.transpose(0, 1).contiguous().view(total_steps, w.batch, 1, w.num_kv_heads, w.head_dim)
+    vnew = vnew.transpose(0, 1).contiguous().view(total_steps, w.batch, 1, w.num_kv_heads, w.head_dim)
     q = torch.randn((total_steps, w.batch, w.num_q_heads, w.head_dim), generator=gen, device=dev).to(torch.float16)
     outs = [torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev) for _ in caches]
     torch.cuda.synchronize()
 
+    # Host mirror of every copy's lengths: per-step algorithmic bytes and whether the
+    # step moves a group out of some sequence's window, known before any step runs.
+    T = [lens0.astype(np.int64) + extra[c] for c in range(copies)]
+    o = 1 if w.sink else 0
+    step_info = []
+    for s in range(total_steps):
+        c = s % copies
+        flush = any(will_flush(int(t), w) for t in T[c])
+        T[c] = T[c] + 1
+        nb = sum(wl.algorithmic_bytes(int(t), 32 * (max(0, int(t) - o - w.residual) // 32), w.bits, w.group,
+                                      w.head_dim) for t in T[c]) * w.num_kv_heads
+        step_info.append((c, flush, nb))
+
     # Timed region: warmup steps, then exactly `steps` steps with only the two
-    # bracketing events (per-step event records cost several microseconds each here).
+    # bracketing events.
     print(f"[bench] {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
-    nbytes = []
     t_start, t_end = ev.create(1)[0], ev.create(1)[0]
     for s in range(args.warmup):
-        c = caches[s % len(caches)]
-        c.step(knew[s], vnew[s], q[s], out=outs[s % len(caches)])
+        c = caches[s % copies]
+        c.step(knew[s], vnew[s], q[s], out=outs[s % copies])
     torch.cuda.synchronize()
     ev.record(t_start, stream)
     host_t0 = time.perf_counter()
-    for s in range(args.warmup, total_steps):
-        c = caches[s % len(caches)]
-        c.step(knew[s], vnew[s], q[s], out=outs[s % len(caches)])
-        nbytes.append(step_bytes(c, w))
+    for s in range(args.warmup, args.warmup + args.steps):
+        c = caches[s % copies]
+        c.step(knew[s], vnew[s], q[s], out=outs[s % copies])
     host_enqueue_s = time.perf_counter() - host_t0
     ev.record(t_end, stream)
     torch.cuda.synchronize()
     total_ms = ev.elapsed_ms(t_start, t_end)
+    timed = step_info[args.warmup:args.warmup + args.steps]
+    bytes_avg = float(np.mean([x[2] for x in timed]))
+    flushes_timed = sum(1 for x in timed if x[1])
+    ms_per_step = total_ms / args.steps
+    value = bytes_avg / (ms_per_step * 1e-3) / 1e9
+
+    # Single steps, each between its own pair of events: steps with a group flush
+    # (a quantize + pack launch before the decode) apart from the others.
+    flush_split = None
+    s0 = args.warmup + args.steps
+    if n_split:
+        es, ee = ev.create(n_split), ev.create(n_split)
+        for i in range(n_split):
+            s = s0 + i
+            c = caches[s % copies]
+            ev.record(es[i], stream)
+            c.step(knew[s], vnew[s], q[s], out=outs[s % copies])
+            ev.record(ee[i], stream)
+        torch.cuda.synchronize()
+        us = np.array([ev.elapsed_ms(es[i], ee[i]) * 1e3 for i in range(n_split)])
+        fl = np.array([step_info[s0 + i][1] for i in range(n_split)])
+        flush_split = {"steps": n_split, "flush_steps": int(fl.sum()),
+                       "no_flush_us_p50": round(float(np.median(us[~fl])), 2) if (~fl).any() else None,
+                       "flush_us_p50": round(float(np.median(us[fl])), 2) if fl.any() else None,
+                       "all_us_p50": round(float(np.median(us)), 2)}
+        ev.destroy(es)
+        ev.destroy(ee)
+    s0 += n_split
 
     # The same step as two library calls (append, then decode), for reference.
-    n2 = min(args.steps, 64)
     torch.cuda.synchronize()
     ev.record(t_start, stream)
     for i in range(n2):
-        s = total_steps + i
-        c = caches[s % len(caches)]
-        c.append(knew2[i], vnew2[i])
-        c.decode(q[i], outs[s % len(caches)])
+        s = s0 + i
+        c = caches[s % copies]
+        c.append(knew[s], vnew[s])
+        c.decode(q[s], outs[s % copies])
     ev.record(t_end, stream)
     torch.cuda.synchronize()
     two_call_us = ev.elapsed_ms(t_start, t_end) / n2 * 1e3
-    bytes_avg = float(np.mean(nbytes))
-    ms_per_step = total_ms / args.steps
-    value = bytes_avg / (ms_per_step * 1e-3) / 1e9
-    out_ok = all(bool(torch.isfinite(o).all()) for o in outs)
+    out_ok = all(bool(torch.isfinite(o_).all()) for o_ in outs)
 
     # Kernel timing: decode calls on the same caches (round-robin, no appends), with
     # HIP events recorded around the split kernel on its stream by the library.
     nk = args.kernel_iters
     ks, ke = ev.create(nk), ev.create(nk)
-    kbytes = []
+    kbytes = [step_bytes(caches[i % copies], w) for i in range(copies)]
     torch.cuda.synchronize()
     for i in range(nk):
-        c = caches[i % len(caches)]
+        c = caches[i % copies]
         c.set_profile_events(ks[i], ke[i])
-        c.decode(q[i % total_steps], outs[i % len(caches)])
-        kbytes.append(step_bytes(c, w))
+        c.decode(q[i % total_steps], outs[i % copies])
     torch.cuda.synchronize()
     for c in caches:
         c.set_profile_events(0, 0)
     kern_ms = np.array([ev.elapsed_ms(ks[i], ke[i]) for i in range(nk)])
     kern_avg_ms = float(np.mean(kern_ms))
-    achieved = float(np.mean(kbytes)) / (kern_avg_ms * 1e-3) / 1e9
+    kbytes_avg = float(np.mean([kbytes[i % copies] for i in range(nk)]))
+    achieved = kbytes_avg / (kern_avg_ms * 1e-3) / 1e9
+    # The whole decode call (split kernel + combine kernel), the scope the FP16-cache
+    # decode is compared at.
+    decode_call_us = time_calls(ev, stream, torch, lambda i: caches[i % copies].decode(q[i % total_steps],
+                                                                                      outs[i % copies]), nk)
 
     # warm (last-level-cache resident) decode of one cache, for reference only
     c = caches[0]
@@ -430,13 +551,18 @@ def main():
             c.close()
         del caches
         torch.cuda.empty_cache()
-        comp = measure_comparisons(torch, kvq, w, ev, stream, dev)
-        comp["quantized_decode_speedup_vs_fp16"] = round(comp["fp16_decode_us"] / (kern_avg_ms * 1e3), 2)
+        comp = measure_comparisons(torch, kvq, w, ev, stream, dev, kbytes_avg)
+        comp["quantized_decode_call_us"] = round(decode_call_us, 2)
+        comp["quantized_vs_fp16_decode_call_speedup"] = round(comp["fp16_decode_call_us"] / decode_call_us, 2)
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w)
+        # the whole workload's step on the CPU, estimated from the sampled heads
+        cpu_step_s = cpu["default_threads"]["step_s_per_head"] * w.batch * w.num_kv_heads
+        cpu["workload_step_s_estimate"] = round(cpu_step_s, 2)
+        cpu["gpu_step_speedup"] = round(cpu_step_s / (ms_per_step * 1e-3), 1)
 
     result = {
         "metric": "2-bit decode-attention µs/step + effective HBM GB/s (% of MI355X peak), 1 GPU",
@@ -456,9 +582,12 @@ def main():
                    "head_dim": w.head_dim, "context": int(w.context_lengths().max()), "bits": w.bits,
                    "group": w.group, "residual": w.residual, "rotate": w.rotate, "sink": w.sink,
                    "pre_rope": w.rope, "page_groups": args.page_groups,
-                   "caches_round_robin": args.copies, "parallelism": "single GPU"},
+                   "caches_round_robin": copies, "extra_prefill_tokens": extra, "parallelism": "single GPU"},
         "step": {"algorithmic_bytes": int(bytes_avg), "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+                 "group_flushes_timed": flushes_timed,
+                 "flush_split": flush_split,
                  "two_call_us_per_step": round(two_call_us, 2),
+                 "decode_call_us": round(decode_call_us, 2),
                  "decode_split_kernel_us": round(kern_avg_ms * 1e3, 2),
                  "decode_split_kernel_p10_p50_p90_us": [round(float(np.percentile(kern_ms, p)) * 1e3, 2)
                                                         for p in (10, 50, 90)],
@@ -469,8 +598,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": f"decode_split_kernel<{w.bits},{w.num_q_heads // w.num_kv_heads}>",
-                     "frac_of_measured_stream_read": (round(achieved / comp["hbm_stream_read_gbps"], 4)
-                                                      if comp else None)},
+                     "limiter": "vector instruction issue and latency (rocprofv3 SQ counters), below the HBM "
+                                "ceiling",
+                     "frac_of_stream_read_2gib": (round(achieved / comp["hbm_stream_read_gbps"], 4)
+                                                  if comp else None),
+                     "frac_of_stream_read_same_bytes": (round(achieved / comp["stream_read_same_bytes_gbps"], 4)
+                                                        if comp else None)},
         "comparison": comp,
         "prefill": prefill,
         "cpu_baseline": cpu,

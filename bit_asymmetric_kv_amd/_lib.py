@@ -104,7 +104,7 @@ def load() -> ctypes.CDLL:
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
     f16p = ctypes.POINTER(KVQFp16Config)
-    lib.kvq_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.kvq_stream_read.argtypes = [vp, sz, vp, i32, vp]
     lib.kvq_fp16_workspace_bytes.argtypes = [f16p, ctypes.POINTER(sz)]
     lib.kvq_fp16_decode_attention.argtypes = [f16p, vp, vp, vp, i64, vp, vp, vp, sz, vp]
     lib.kvq_fp16_decode_attention_noalloc.argtypes = [f16p, vp, vp, vp, i64, vp, vp, vp]
@@ -298,11 +298,16 @@ class KVCache:
 # -- comparison kernels -------------------------------------------------------
 
 def stream_read(buf, fold):
-    """Stream-read every byte of the device tensor `buf` once; xor a fold into the
-    int32 device tensor `fold` (one element). Asynchronous on the current stream."""
+    """Stream-read every byte of the device tensor `buf` once with one workgroup per
+    element of the int32 device tensor `fold`, which receives their xor folds (the xor
+    of all elements equals the xor of every 32-bit word of `buf`). Asynchronous on the
+    current stream."""
     import torch
+    if fold.dtype != torch.int32 or not fold.is_contiguous() or not fold.is_cuda:
+        raise ValueError("fold must be a contiguous int32 device tensor")
     check(load().kvq_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
-                                 ctypes.c_void_p(fold.data_ptr()), ctypes.c_void_p(_stream_ptr(torch, buf.device))))
+                                 ctypes.c_void_p(fold.data_ptr()), int(fold.numel()),
+                                 ctypes.c_void_p(_stream_ptr(torch, buf.device))))
 
 
 class Fp16Decode:

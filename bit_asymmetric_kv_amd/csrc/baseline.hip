@@ -32,7 +32,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Reads every 16-byte word of buf[0, n16) once (grid-stride, four words in flight
 // per thread, nontemporal loads: the data is not reused), folds the words with xor
-// and publishes one word per workgroup into *fold so the loads stay live.
+// and stores workgroup i's fold in fold[i], so the loads stay live without any
+// atomic (one word per workgroup: no serialized read-modify-write at the end).
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf, size_t n16,
                                                           uint32_t* __restrict__ fold) {
   uint32_t acc = 0;
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   __shared__ uint32_t red[4];
   if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) atomicXor(fold, red[0] ^ red[1] ^ red[2] ^ red[3]);
+  if (threadIdx.x == 0) fold[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
 struct Fp16Args {

@@ -604,24 +604,18 @@ kvq_status kvq_reset_sequence(kvq_cache* c, int32_t b) {
   return ok();
 }
 
-kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* fold, hipStream_t stream) {
+kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* fold, int32_t fold_words, hipStream_t stream) {
   if (!buf || !fold) return fail(KVQ_ERR_INVALID_ARG, "buf and fold must be device pointers");
   if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
     return fail(KVQ_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and buf 16-byte aligned");
-  int ndev = 0, dev = 0, cus = 0;
+  if (fold_words < 1 || fold_words > kvq::kMaxStreamWorkgroups)
+    return fail(KVQ_ERR_INVALID_ARG, "fold_words must be in [1, %d] (got %d)", kvq::kMaxStreamWorkgroups, fold_words);
+  int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
     (void)hipGetLastError();
     return fail(KVQ_ERR_NO_DEVICE, "no HIP device available");
   }
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return fail(KVQ_ERR_HIP, "device query failed: %s", hipGetErrorString(hipGetLastError()));
-  const size_t n16 = bytes / 16;
-  // 64 workgroups per compute unit keep enough loads in flight (measured sweep);
-  // fewer for small buffers, at least four words per thread.
-  const size_t want = (n16 + 4 * 256 - 1) / (4 * 256);
-  const int blocks = int(std::max<size_t>(1, std::min<size_t>(want, size_t(cus) * 64)));
-  const hipError_t e = kvq::launch_stream_read(buf, bytes, fold, blocks, stream);
+  const hipError_t e = kvq::launch_stream_read(buf, bytes, fold, fold_words, stream);
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "stream read launch failed: %s", hipGetErrorString(e));
   return ok();
 }

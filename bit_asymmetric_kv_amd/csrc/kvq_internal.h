@@ -158,6 +158,7 @@ hipError_t launch_fp16_decode(const void* k, const void* v, const int32_t* lens,
                               int Hkv, float scale_log2, const void* q, float* out, float* part, int nsplit,
                               int cps, hipStream_t stream);
 constexpr int kFp16MaxSplits = 1024;
+constexpr int kMaxStreamWorkgroups = 1 << 16;  // streaming-read probe: one fold word per workgroup
 // The FP16-cache decode's static scratch (partials of the variant that allocates
 // nothing): 4 MiB per GPU, room for 8065 partials of 520 bytes.
 constexpr size_t kFp16ScratchBytes = size_t(4) << 20;

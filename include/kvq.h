@@ -219,13 +219,15 @@ const char* kvq_last_error(void);
 /* ---- Comparison kernels (measured beside the quantized path, not part of it) ---- */
 
 /* Streaming-read probe: reads each 16-byte word of the device buffer buf[0, bytes)
- * once with vector loads spread over the whole GPU and xors a fold of the words
- * into the device word *fold (the caller clears it first if it wants the fold), so
- * the loads cannot be elided. Timing it gives the achievable HBM read bandwidth to
- * set the decode kernel's effective bandwidth against (the nominal peak is a
- * datasheet figure). bytes: positive multiple of 16; buf 16-byte aligned.
- * Asynchronous on `stream`. */
-kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* fold, hipStream_t stream);
+ * once with vector loads spread over the whole GPU, in fold_words workgroups of 256
+ * threads (1 .. 65536; a few per compute unit keep enough loads in flight), and
+ * stores in fold[i] the xor of the 32-bit words workgroup i read, so the loads
+ * cannot be elided: the xor of fold[0 .. fold_words) equals the xor of every word of
+ * the buffer. fold is a device array of fold_words uint32 words, wholly written.
+ * Timing it gives the achievable HBM read bandwidth to set the decode kernel's
+ * effective bandwidth against (the nominal peak is a datasheet figure). bytes:
+ * positive multiple of 16; buf 16-byte aligned. Asynchronous on `stream`. */
+kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* fold, int32_t fold_words, hipStream_t stream);
 
 /* Decode attention over a plain FP16 KV cache, the full-precision decode that the
  * pages set low-bit caches against (flash-decoding over the whole cache: "Read

@@ -160,7 +160,9 @@ def test_comparison_entry_points_validate_on_the_host():
     # null pointers
     assert lib.kvq_fp16_decode_attention(ctypes.byref(cfg), None, fake, fake, 100, fake, fake, fake, 1 << 30,
                                          None) == _lib.KVQ_ERR_INVALID_ARG
-    # stream read: size not a multiple of 16, misaligned buffer, null fold word
-    assert lib.kvq_stream_read(fake, 100, fake, None) == _lib.KVQ_ERR_INVALID_ARG
-    assert lib.kvq_stream_read(ctypes.c_void_p(264), 1024, fake, None) == _lib.KVQ_ERR_INVALID_ARG
-    assert lib.kvq_stream_read(fake, 1024, None, None) == _lib.KVQ_ERR_INVALID_ARG
+    # stream read: size not a multiple of 16, misaligned buffer, null fold array, fold words out of range
+    assert lib.kvq_stream_read(fake, 100, fake, 64, None) == _lib.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_stream_read(ctypes.c_void_p(264), 1024, fake, 64, None) == _lib.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_stream_read(fake, 1024, None, 64, None) == _lib.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_stream_read(fake, 1024, fake, 0, None) == _lib.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_stream_read(fake, 1024, fake, (1 << 16) + 1, None) == _lib.KVQ_ERR_INVALID_ARG

@@ -19,17 +19,19 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("words", [4, 4 * 1000 + 4, 4 * (1 << 20) + 12])
-def test_stream_read_fold(dev, words):
+@pytest.mark.parametrize("words,workgroups", [(4, 1), (4, 7), (4 * 1000 + 4, 33), (4 * (1 << 20) + 12, 2048)])
+def test_stream_read_fold(dev, words, workgroups):
     import bit_asymmetric_kv_amd as kvq
     rng = np.random.default_rng(words)
     host = rng.integers(0, 2**32, size=words, dtype=np.uint32)
     buf = torch.from_numpy(host.view(np.int32)).to(dev)
-    fold = torch.zeros(1, dtype=torch.int32, device=dev)
-    print(f"case stream_read words={words}", flush=True)
+    # every word of the fold array is written (the poison must not survive)
+    fold = torch.full((workgroups,), 0x5A5A5A5A, dtype=torch.int32, device=dev)
+    print(f"case stream_read words={words} workgroups={workgroups}", flush=True)
     kvq.stream_read(buf, fold)
     torch.cuda.synchronize()
-    assert int(fold.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host))
+    got = int(np.bitwise_xor.reduce(fold.cpu().numpy().view(np.uint32)))
+    assert got == int(np.bitwise_xor.reduce(host))
 
 
 def _fp16_case(dev, B, Hq, Hkv, lens, t_cap, seed, scale=0.0):
