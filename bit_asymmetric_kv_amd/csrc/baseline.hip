@@ -27,6 +27,8 @@ constexpr int kWaves = 4;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -68,123 +70,176 @@ struct Fp16Args {
   float scale_log2;
 };
 
-// Online-softmax state of one wave for HG query heads: max m and sum l (log2
-// domain, identical in every lane) and the unnormalized output of channels
-// 2 lane, 2 lane + 1.
+// One workgroup per (split of cps chunks of 32 tokens, kv-head, sequence); its four
+// waves take the split's chunks in turn (wave w: chunks w, w + 4, ...). A wave holds
+// one chunk in registers and issues the next chunk's key loads as soon as its score
+// MFMAs have read the keys and its value loads as soon as the weighted sum has read
+// the values; the many resident waves keep enough loads in flight.
+//
+// Scores: an MFMA 16x16x32 f16 contraction over channels with the keys as A (token
+// rows straight from the cache, exact fp16) and the query as B (exact fp16), one
+// MFMA column per head (copies fill the 16 columns), fp32 accumulation; the softmax
+// scale is applied to the fp32 scores. Lane (column c, row block kb) then holds the
+// scores of head c % HG for tokens 4 kb + i and 16 + 4 kb + i (i < 4).
+// Weighted values: lane l accumulates channels 4 (l % 32) .. + 3 over the chunk's
+// tokens 2 i + l / 32 (8 bytes per token: a half-wave reads one 256-byte row) for
+// every head, with fused multiply-adds in fp32; the softmax weights of all heads
+// reach the lanes through the wave's shared memory. The two half-waves' sums are
+// added once, after the wave's last chunk.
 template <int HG>
-struct Fp16State {
-  float m[HG], l[HG], o0[HG], o1[HG];
-};
-
-// Attention over tokens [t0, t0 + cnt) (cnt in 1..32) of one (sequence, kv-head):
-// lane l scores token l % 32 over channel half l / 32, then every lane accumulates
-// its two channels over the chunk's tokens.
-template <int HG>
-__device__ void fp16_chunk(const __half* krow0, const __half* vrow0, int cnt, const float (*qf)[kD],
-                           Fp16State<HG>& st, int lane) {
-  const int tl = lane % 32, hf = lane / 32;
-  const bool kval = tl < cnt;
-  uint4 kr[8];
-  {
-    const uint4* kp = reinterpret_cast<const uint4*>(krow0 + size_t(kval ? tl : 0) * kD + 64 * hf);
-    for (int i = 0; i < 8; i++) kr[i] = kp[i];
-  }
-  uint32_t vr[kChunk];
-  for (int t = 0; t < kChunk; t++)
-    vr[t] = *reinterpret_cast<const uint32_t*>(vrow0 + size_t(t < cnt ? t : 0) * kD + 2 * lane);
-  float x[HG];
-  for (int hh = 0; hh < HG; hh++) x[hh] = 0.0f;
-  for (int i = 0; i < 8; i++) {
-    // The query rows stay in shared memory: without this barrier the compiler hoists
-    // all of their loads out of the chunk loop into registers.
-    asm volatile("" ::: "memory");
-    const half8 k8 = __builtin_bit_cast(half8, kr[i]);
-    for (int e = 0; e < 8; e++) {
-      const float kv = float(k8[e]);
-      for (int hh = 0; hh < HG; hh++) x[hh] = __builtin_fmaf(qf[hh][64 * hf + 8 * i + e], kv, x[hh]);
-    }
-  }
-  float p[HG];
-  for (int hh = 0; hh < HG; hh++) {
-    const float xs = x[hh] + __shfl_xor(x[hh], 32);
-    const float sc = kval ? xs : -INFINITY;
-    float cm = sc;
-    for (int off = 16; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
-    const float mn = fmaxf(st.m[hh], cm);
-    const float alpha = st.m[hh] == -INFINITY ? 0.0f : exp2f(st.m[hh] - mn);
-    p[hh] = kval ? exp2f(sc - mn) : 0.0f;
-    float ls = p[hh];
-    for (int off = 16; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
-    st.l[hh] = st.l[hh] * alpha + ls;
-    st.o0[hh] *= alpha;
-    st.o1[hh] *= alpha;
-    st.m[hh] = mn;
-  }
-  for (int t = 0; t < kChunk; t++) {
-    if (t < cnt) {
-      const half2v vv = __builtin_bit_cast(half2v, vr[t]);
-      const float v0 = float(vv[0]), v1 = float(vv[1]);
-      for (int hh = 0; hh < HG; hh++) {
-        const float pt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[hh]), t));
-        st.o0[hh] = __builtin_fmaf(pt, v0, st.o0[hh]);
-        st.o1[hh] = __builtin_fmaf(pt, v1, st.o1[hh]);
-      }
-    }
-  }
-}
-
-// One workgroup per (split of cps chunks, kv-head, sequence); its four waves take
-// contiguous quarters of the split, and their states are merged into the split's
-// partial (m, l, o[128]) per query head.
-template <int HG>
-__global__ __launch_bounds__(256) void fp16_split_kernel(Fp16Args a) {
-  __shared__ float qf[HG][kD];
-  __shared__ float wpart[kWaves][HG][kPartialStride];
+__global__ __launch_bounds__(256, HG == 8 ? 1 : 2) void fp16_split_kernel(Fp16Args a) {
+  __shared__ float pst[kWaves][kChunk][HG];               // softmax weights of the current chunk
+  __shared__ float wpart[kWaves][HG][kPartialStride];     // per-wave partials
   const int split = blockIdx.x % a.nsplit;
   const int h = (blockIdx.x / a.nsplit) % a.Hkv;
   const int b = blockIdx.x / (a.nsplit * a.Hkv);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int col = lane % 16, kb = lane / 16, hc = col % HG;
+  const int vc = lane % 32, vh = lane / 32;  // value channels 4 vc .. + 3, tokens 2 i + vh
   const int T = int(min<long long>(a.lens[b], a.t_cap));
   const int nch = (T + kChunk - 1) / kChunk;
-
-  for (int e = threadIdx.x; e < HG * kD; e += blockDim.x)
-    qf[e / kD][e % kD] = __half2float(a.q[(size_t(b) * a.Hq + h * HG + e / kD) * kD + e % kD]) * a.scale_log2;
-  __syncthreads();
-
   const int c0 = split * a.cps, c1 = min(nch, c0 + a.cps);
-  const int per = (max(0, c1 - c0) + kWaves - 1) / kWaves;
-  const int wc0 = c0 + wave * per, wc1 = min(c1, wc0 + per);
-  Fp16State<HG> st;
-  for (int hh = 0; hh < HG; hh++) {
-    st.m[hh] = -INFINITY;
-    st.l[hh] = st.o0[hh] = st.o1[hh] = 0.0f;
-  }
+  const int len = max(0, c1 - c0);
+  const int n = __builtin_amdgcn_readfirstlane(max(0, (len - wave + kWaves - 1) / kWaves));
   const size_t row0 = (size_t(b) * a.Hkv + h) * size_t(a.t_cap);
-  for (int c = wc0; c < wc1; c++) {
-    const int t0 = c * kChunk;
-    fp16_chunk<HG>(a.k + (row0 + t0) * kD, a.v + (row0 + t0) * kD, min(kChunk, T - t0), qf, st, lane);
-  }
-  for (int hh = 0; hh < HG; hh++) {
-    wpart[wave][hh][2 + 2 * lane] = st.o0[hh];
-    wpart[wave][hh][3 + 2 * lane] = st.o1[hh];
-    if (lane == 0) {
-      wpart[wave][hh][0] = st.m[hh];
-      wpart[wave][hh][1] = st.l[hh];
+  const __half* kbase = a.k + row0 * kD;
+  const __half* vbase = a.v + row0 * kD;
+
+  auto chunk_start = [&](int r) { return (c0 + wave + kWaves * r) * kChunk; };
+  uint4 kr[8];   // kr[2 kc + tile]: key row 16 tile + col, channels 32 kc + 8 kb .. + 7
+  uint2 vr[16];  // vr[i]: value row 2 i + vh, channels 4 vc .. + 3
+  auto load_keys = [&](int r) {
+    const int t0 = chunk_start(r);
+    for (int tile = 0; tile < 2; tile++)
+      for (int kc = 0; kc < 4; kc++) {
+        const int t = min(t0 + 16 * tile + col, T - 1);  // rows past the end re-read the last one
+        kr[2 * kc + tile] = *reinterpret_cast<const uint4*>(kbase + size_t(t) * kD + 32 * kc + 8 * kb);
+      }
+  };
+  auto load_values = [&](int r) {
+    const int t0 = chunk_start(r);
+    for (int i = 0; i < 16; i++) {
+      const int t = min(t0 + 2 * i + vh, T - 1);
+      vr[i] = *reinterpret_cast<const uint2*>(vbase + size_t(t) * kD + 4 * vc);
     }
+  };
+  if (n > 0) {
+    load_keys(0);
+    load_values(0);
+  }
+
+  // query of head hc as the MFMA B operand (channels 32 kc + 8 kb .. + 7)
+  half8 qb[4];
+  {
+    const __half* qrow = a.q + (size_t(b) * a.Hq + h * HG + hc) * kD;
+    for (int kc = 0; kc < 4; kc++)
+      qb[kc] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(qrow + 32 * kc + 8 * kb));
+  }
+
+  float m[HG];         // running max per head (log2 units), the same in every lane
+  float l_col = 0.0f;  // sum of this lane's weights of head hc
+  float o[HG][4];      // this lane's channels, over its half-wave's tokens
+  for (int hh = 0; hh < HG; hh++) {
+    m[hh] = -INFINITY;
+    for (int c = 0; c < 4; c++) o[hh][c] = 0.0f;
+  }
+
+  for (int r = 0; r < n; r++) {
+    const int t0 = chunk_start(r);
+    float4v s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
+    for (int kc = 0; kc < 4; kc++) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, kr[2 * kc]), qb[kc], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, kr[2 * kc + 1]), qb[kc], s1, 0, 0, 0);
+    }
+    if (r + 1 < n) load_keys(r + 1);
+    float x[8];
+    float mx = -INFINITY;
+    for (int i = 0; i < 8; i++) {
+      const int tk = i < 4 ? 4 * kb + i : 16 + 4 * kb + (i - 4);
+      const float sv = i < 4 ? s0[i] : s1[i - 4];
+      x[i] = t0 + tk < T ? sv * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));  // chunk max of head hc (every chunk holds a valid token)
+    float alpha[HG];
+    bool grew = false;
+    for (int hh = 0; hh < HG; hh++) {
+      const float mh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hh));
+      const float mn = fmaxf(m[hh], mh);
+      alpha[hh] = m[hh] == -INFINITY ? 0.0f : exp2f(m[hh] - mn);
+      grew = grew || mn != m[hh];
+      m[hh] = mn;
+    }
+    float mcol = m[0], acol = alpha[0];
+    for (int hh = 1; hh < HG; hh++) {
+      mcol = hc == hh ? m[hh] : mcol;
+      acol = hc == hh ? alpha[hh] : acol;
+    }
+    float ps = 0.0f;
+    for (int i = 0; i < 8; i++) {
+      const int tk = i < 4 ? 4 * kb + i : 16 + 4 * kb + (i - 4);
+      x[i] = exp2f(x[i] - mcol);
+      ps += x[i];
+      if (col < HG) pst[wave][tk][col] = x[i];
+    }
+    l_col = l_col * acol + ps;
+    if (grew)
+      for (int hh = 0; hh < HG; hh++)
+        for (int c = 0; c < 4; c++) o[hh][c] *= alpha[hh];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = 0; i < 16; i++) {
+      // at most four tokens' weights in registers at a time (the compiler would
+      // otherwise read all 16 x HG of them up front)
+      if (i % 4 == 0) asm volatile("" ::: "memory");
+      float pw[HG];
+      for (int hh = 0; hh < HG; hh++) pw[hh] = pst[wave][2 * i + vh][hh];
+      const half4v v4 = __builtin_bit_cast(half4v, vr[i]);
+      for (int c = 0; c < 4; c++) {
+        const float vf = float(v4[c]);
+        for (int hh = 0; hh < HG; hh++) o[hh][c] = __builtin_fmaf(vf, pw[hh], o[hh][c]);
+      }
+    }
+    // the next chunk's values go into the registers this chunk's have just left
+    asm volatile("" ::: "memory");
+    if (r + 1 < n) load_values(r + 1);
+    // the weights are read before the next chunk overwrites them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // sums over the two half-waves (values) and the four row blocks (weights); lanes
+  // 0..31 write the wave's partial
+  for (int hh = 0; hh < HG; hh++)
+    for (int c = 0; c < 4; c++) o[hh][c] += __shfl_xor(o[hh][c], 32);
+  float lt = l_col + __shfl_xor(l_col, 16);
+  lt += __shfl_xor(lt, 32);
+  if (vh == 0) {
+    for (int hh = 0; hh < HG; hh++)
+      for (int c = 0; c < 4; c++) wpart[wave][hh][2 + 4 * vc + c] = o[hh][c];
+  }
+  if (kb == 0 && col < HG) {
+    float mc = m[0];
+    for (int hh = 1; hh < HG; hh++) mc = col == hh ? m[hh] : mc;
+    wpart[wave][col][0] = mc;
+    wpart[wave][col][1] = lt;
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < HG * kPartialStride; idx += blockDim.x) {
     const int hh = idx / kPartialStride, c = idx % kPartialStride;
     float M = -INFINITY;
     for (int w = 0; w < kWaves; w++) M = fmaxf(M, wpart[w][hh][0]);
-    float r = 0.0f;
+    float res = 0.0f;
     if (c == 0) {
-      r = M;
+      res = M;
     } else if (M != -INFINITY) {
       for (int w = 0; w < kWaves; w++)
-        if (wpart[w][hh][0] != -INFINITY) r += wpart[w][hh][c] * exp2f(wpart[w][hh][0] - M);
+        if (wpart[w][hh][0] != -INFINITY) res += wpart[w][hh][c] * exp2f(wpart[w][hh][0] - M);
     }
-    a.part[((size_t(b) * a.Hq + h * HG + hh) * a.nsplit + split) * kPartialStride + c] = r;
+    a.part[((size_t(b) * a.Hq + h * HG + hh) * a.nsplit + split) * kPartialStride + c] = res;
   }
 }
 

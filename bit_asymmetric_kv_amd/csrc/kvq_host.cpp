@@ -670,10 +670,11 @@ kvq_status plan_fp16(const kvq_fp16_config* cfg, int64_t max_len, Fp16Plan& p) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(KVQ_ERR_HIP, "device query failed: %s", hipGetErrorString(hipGetLastError()));
-  // About four workgroups per compute unit in one round, at least one chunk per wave.
+  // Two workgroups per compute unit (the kernel's occupancy) in one round, at least
+  // one chunk per wave.
   const int64_t bh = int64_t(cfg->batch) * cfg->num_kv_heads;
   const int64_t nch = (max_len + 31) / 32;
-  int64_t splits = std::max<int64_t>(1, (int64_t(cus) * 4) / bh);
+  int64_t splits = std::max<int64_t>(1, (int64_t(cus) * 2) / bh);
   int64_t cps = std::max<int64_t>(4, (nch + splits - 1) / splits);
   int64_t nsplit = (nch + cps - 1) / cps;
   if (nsplit > kvq::kFp16MaxSplits) {
