@@ -756,6 +756,11 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
   // high and low parts, two MFMAs each. The group's scale / zero-point region and
   // its start angle's cos / sin come through this wave's shared memory.
   auto key_rope = [&](const GroupRegs<BITS, NJ>& g, float4v& r0, float4v& r1) {
+    // The low parts' residuals x - hi come from one mixed-precision fused operation
+    // (fp16 hi times -1 plus the fp32 x; exact, since hi is x truncated to fp16); the
+    // opaque -1 keeps the compiler from rewriting it as a conversion and a subtraction.
+    float neg1 = -1.0f;
+    asm("" : "+v"(neg1));
     uint4* wl = ropew + wave * 64;
     wl[lane] = __builtin_bit_cast(uint4, g.ks);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -778,7 +783,7 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
         float qr[8], rr[8];
         for (int e = 0; e < 8; e++) qr[e] = __builtin_fmaf(qpair[e], sn[e], qreg[it][e] * cs[e]);
         const half8 hi = to_half8(qr);
-        for (int e = 0; e < 8; e++) rr[e] = qr[e] - float(hi[e]);
+        for (int e = 0; e < 8; e++) rr[e] = __builtin_fmaf(float(hi[e]), neg1, qr[e]);
         const half8 lo = to_half8_rne(rr);
         if (bwriter) {
           const int rot = (U / 2) * (cb % 4);
@@ -822,8 +827,8 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
         const half8 ah = to_half8(ya), bh = to_half8(yb);
         float ra[8], rb[8];
         for (int s2 = 0; s2 < 8; s2++) {
-          ra[s2] = ya[s2] - float(ah[s2]);
-          rb[s2] = yb[s2] - float(bh[s2]);
+          ra[s2] = __builtin_fmaf(float(ah[s2]), neg1, ya[s2]);
+          rb[s2] = __builtin_fmaf(float(bh[s2]), neg1, yb[s2]);
         }
         const half8 al = to_half8_rne(ra), bl = to_half8_rne(rb);
         float4v r = tile == 0 ? r0 : r1;
