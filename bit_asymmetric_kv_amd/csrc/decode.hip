@@ -312,6 +312,11 @@ __device__ void merge_and_store(const DecodeArgs& a, int b, int h, int split, co
 // With pre-RoPE keys (ROPE), the keys of a chunk starting at a group start position
 // (rope_entry >= 0: the position's entry in a.rope_tab) are rotated after loading:
 // lane l pairs its channel with the same token's channel 64 away, held by lane l^32.
+// Row stride (floats) of the in-group rotary table in shared memory: one 16-byte
+// pad per row moves consecutive rows to different banks (lanes read one column of
+// 16 different rows at once).
+constexpr int kRopeRow = kD + 4;
+
 template <int HG, bool ROPE>
 __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt, int s0, int wlim, int t_old,
                              const float (*qf)[kD], const float* expo, const WaveParts& wp, int wave, int lane,
@@ -359,7 +364,7 @@ __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt,
     if (rope_entry >= 0) {
       // angle (t0 + tl) theta_f = base angle of t0 plus in-group angle of tl
       const float* bt = a.rope_tab + size_t(rope_entry) * kD;
-      const float* it = ropein + tl * kD;
+      const float* it = ropein + tl * kRopeRow;
       for (int d = 0; d < 64; d++) {
         const float xp = __shfl_xor(kf[d], 32);
         const float c = bt[d] * it[d] - bt[64 + d] * it[64 + d];
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
   __shared__ float pstage[NR > 1 ? kWaves : 1][4][HG][8];
   // Pre-RoPE keys: in-group rotary cos / sin [32][128], and per wave the current
   // group's key scales / zero-points (512 B) and base-angle cos / sin (512 B).
-  __shared__ float ropein[ROPE ? kG * kD : 1];
+  __shared__ float ropein[ROPE ? kG * kRopeRow : 1];
   __shared__ uint4 ropew[ROPE ? kWaves * 64 : 1];
   const WaveParts wp{wpart_mem, HG * kPartialStride};
 
@@ -593,7 +598,8 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
 
   if constexpr (ROPE) {
     for (int e = threadIdx.x; e < kG * kD / 4; e += blockDim.x)
-      reinterpret_cast<float4*>(ropein)[e] = reinterpret_cast<const float4*>(a.rope_in)[e];
+      reinterpret_cast<float4*>(ropein)[(e / (kD / 4)) * (kRopeRow / 4) + e % (kD / 4)] =
+          reinterpret_cast<const float4*>(a.rope_in)[e];
     __syncthreads();
   }
 
@@ -806,7 +812,7 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
       const half8 bka = sh.bk[wave].b[kc][kb][(u + (U / 2) * kb) % U];
       const half8 bkb = sh.bk[wave].b[kc + 2][kb][(u + (U / 2) * kb) % U];
       for (int tile = 0; tile < 2; tile++) {
-        const float* it = ropein + (16 * tile + lane % 16) * kD;
+        const float* it = ropein + (16 * tile + lane % 16) * kRopeRow;
         const half8 ca = code_operand<BITS>(g.kc0, g.kc1, 2 * kc + tile);
         const half8 cb = code_operand<BITS>(g.kc0, g.kc1, 2 * (kc + 2) + tile);
         float ya[8], yb[8];
