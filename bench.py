@@ -16,10 +16,12 @@ algorithmic bytes (packed codes + fp16 scales/zero-points + fp16 window) divided
 by the step time, measured over the timed steps with one pair of HIP events
 bracketing them (no per-step records). `roofline` reports the dominant kernel (the
 decode split kernel), timed in a second pass of decode calls on the same caches
-with HIP events that the library records around that kernel on its own stream.
-Every event is created without the system-scope fence (hipEventDisableSystemFence):
-a default event record writes back and invalidates the caches, which costs several
-microseconds per record and lengthens the kernel it brackets.
+with HIP events that the library attaches to that kernel's launch
+(hipExtLaunchKernelGGL): they carry the kernel's own start and end timestamps, as a
+kernel trace reports them. Every event is created without the system-scope fence
+(hipEventDisableSystemFence): a default event record writes back and invalidates the
+caches, which costs several microseconds per record and lengthens the kernel it
+brackets.
 
 Steady state: cache c is prefilled with a few extra tokens (under 32) so that, when
 the timed steps start, it sits 31 - 32 c / copies appends past its last group flush;
@@ -179,7 +181,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(w, heads=2, steps=4):
+def cpu_baseline(w, heads=4, steps=12):
     """Time the CPU oracle on `heads` KV heads of sequence 0 at the workload's full
     context, twice: with numpy / BLAS at their default thread count and pinned to one
     thread. Per run: the prefill (quantize the whole prompt), then `steps` steps of
@@ -330,22 +332,34 @@ def _counter_per_dispatch(path, kernel_substr, counter):
 
 def summarize_traffic(dec_fetch, dec_write, copy_fetch, copy_write, workload, out_path):
     """HBM bytes per decode split launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
-    each scaled by the same counter's reading for the calibration copy."""
+    each scaled by the same counter's reading for the calibration copy. The result is
+    merged into out_path under workloads[workload]; the copy's readings are stored
+    once under "calibration" ("-" for copy_fetch and copy_write reuses them)."""
+    data = {"calibration": None, "workloads": {}}
+    if os.path.exists(out_path):
+        with open(out_path) as f:
+            old = json.load(f)
+        if "workloads" in old:
+            data = old
+    if copy_fetch == "-" or copy_write == "-":
+        cal = data["calibration"]
+        if cal is None:
+            raise SystemExit(f"{out_path} holds no calibration copy readings")
+    else:
+        f_cp, _ = _counter_per_dispatch(copy_fetch, "copy", "FETCH_SIZE")
+        w_cp, _ = _counter_per_dispatch(copy_write, "copy", "WRITE_SIZE")
+        cal = {"copy_bytes": COPY_BYTES, "copy_fetch_kib": f_cp, "copy_write_kib": w_cp,
+               "fetch_scale": COPY_BYTES / (f_cp * 1024.0), "write_scale": COPY_BYTES / (w_cp * 1024.0)}
+        data["calibration"] = cal
     f_dec, n1 = _counter_per_dispatch(dec_fetch, "decode_split_kernel", "FETCH_SIZE")
     w_dec, n2 = _counter_per_dispatch(dec_write, "decode_split_kernel", "WRITE_SIZE")
-    f_cp, _ = _counter_per_dispatch(copy_fetch, "copy", "FETCH_SIZE")
-    w_cp, _ = _counter_per_dispatch(copy_write, "copy", "WRITE_SIZE")
-    f_scale = COPY_BYTES / (f_cp * 1024.0)
-    w_scale = COPY_BYTES / (w_cp * 1024.0)
-    res = {"workload": workload,
-           "bytes_per_launch": int(f_dec * 1024 * f_scale + w_dec * 1024 * w_scale),
-           "fetch_kib_per_dispatch": f_dec, "write_kib_per_dispatch": w_dec,
-           "copy_fetch_kib": f_cp, "copy_write_kib": w_cp, "copy_bytes": COPY_BYTES,
-           "fetch_scale": f_scale, "write_scale": w_scale, "dispatches": [n1, n2],
+    res = {"bytes_per_launch": int(f_dec * 1024 * cal["fetch_scale"] + w_dec * 1024 * cal["write_scale"]),
+           "fetch_kib_per_dispatch": f_dec, "write_kib_per_dispatch": w_dec, "dispatches": [n1, n2],
            "kernel_source_sha256": kernel_source_hash()}
+    data["workloads"][workload] = res
     with open(out_path, "w") as f:
-        json.dump(res, f, indent=1)
-    print(json.dumps(res))
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps({workload: res}))
 
 
 def main():
@@ -498,7 +512,7 @@ def main():
     out_ok = all(bool(torch.isfinite(o_).all()) for o_ in outs)
 
     # Kernel timing: decode calls on the same caches (round-robin, no appends), with
-    # HIP events recorded around the split kernel on its stream by the library.
+    # HIP events that the library attaches to the split kernel's launch.
     nk = args.kernel_iters
     ks, ke = ev.create(nk), ev.create(nk)
     kbytes = [step_bytes(caches[i % copies], w) for i in range(copies)]
@@ -539,7 +553,8 @@ def main():
             with open(args.traffic_json) as f:
                 t = json.load(f)
             # counters taken on another build of the kernel no longer describe it
-            if t.get("workload") == w.name and t.get("kernel_source_sha256") == kernel_source_hash():
+            t = t.get("workloads", {}).get(w.name, {})
+            if t.get("kernel_source_sha256") == kernel_source_hash():
                 traffic = t.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
@@ -597,7 +612,8 @@ def main():
                  "outputs_finite": out_ok},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": f"decode_split_kernel<{w.bits},{w.num_q_heads // w.num_kv_heads}>",
+                     "kernel": (f"decode_split_kernel<{w.bits},{w.num_q_heads // w.num_kv_heads},"
+                                f"{'true' if w.rope else 'false'}>"),
                      "limiter": "vector instruction issue and latency (rocprofv3 SQ counters), below the HBM "
                                 "ceiling",
                      "frac_of_stream_read_2gib": (round(achieved / comp["hbm_stream_read_gbps"], 4)

@@ -28,6 +28,7 @@
 //    columns); the value zero-points enter through sum_t p_t z_t per channel group.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include "kvq_internal.h"
 
@@ -1082,11 +1083,21 @@ int resident_blocks_of() {
   return per_cu;
 }
 
+// With profiling events the launch goes through hipExtLaunchKernelGGL, which sets the
+// events to the kernel's own start and end timestamps (those of its dispatch packet,
+// as a kernel trace reports them). Events recorded on the stream around the launch
+// would instead take their start stamp as soon as the previous kernel was dispatched,
+// so the interval would include the tail of that kernel.
 template <int BITS, int HG, bool ROPE>
-hipError_t launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
+hipError_t launch_split(const DecodeArgs& a, int B, hipStream_t stream, hipEvent_t prof_start,
+                        hipEvent_t prof_stop) {
   const int nsplit_total = a.plan.use_prefix ? a.plan.prefix[B] : B * a.plan.uniform;
-  hipLaunchKernelGGL((decode_split_kernel<BITS, HG, ROPE>), dim3((nsplit_total + B * a.wblocks) * a.Hkv), dim3(256), 0,
-                     stream, a);
+  const dim3 grid((nsplit_total + B * a.wblocks) * a.Hkv);
+  if (prof_start || prof_stop)
+    hipExtLaunchKernelGGL((decode_split_kernel<BITS, HG, ROPE>), grid, dim3(256), 0, stream, prof_start, prof_stop, 0,
+                          a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<BITS, HG, ROPE>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1149,16 +1160,20 @@ int device_compute_units() {
   return cus;
 }
 
+template <int BITS, bool ROPE>
+hipError_t launch_split_hg(const DecodeArgs& a, int hg, int B, hipStream_t stream, hipEvent_t ps, hipEvent_t pe) {
+  return hg == 1   ? launch_split<BITS, 1, ROPE>(a, B, stream, ps, pe)
+         : hg == 2 ? launch_split<BITS, 2, ROPE>(a, B, stream, ps, pe)
+         : hg == 4 ? launch_split<BITS, 4, ROPE>(a, B, stream, ps, pe)
+                   : launch_split<BITS, 8, ROPE>(a, B, stream, ps, pe);
+}
+
 template <bool ROPE>
-hipError_t launch_split_for(const DecodeArgs& a, int bits, int hg, int B, hipStream_t stream) {
-  if (bits == 2)
-    return hg == 1 ? launch_split<2, 1, ROPE>(a, B, stream) : hg == 2 ? launch_split<2, 2, ROPE>(a, B, stream)
-           : hg == 4 ? launch_split<2, 4, ROPE>(a, B, stream) : launch_split<2, 8, ROPE>(a, B, stream);
-  if (bits == 3)
-    return hg == 1 ? launch_split<3, 1, ROPE>(a, B, stream) : hg == 2 ? launch_split<3, 2, ROPE>(a, B, stream)
-           : hg == 4 ? launch_split<3, 4, ROPE>(a, B, stream) : launch_split<3, 8, ROPE>(a, B, stream);
-  return hg == 1 ? launch_split<4, 1, ROPE>(a, B, stream) : hg == 2 ? launch_split<4, 2, ROPE>(a, B, stream)
-         : hg == 4 ? launch_split<4, 4, ROPE>(a, B, stream) : launch_split<4, 8, ROPE>(a, B, stream);
+hipError_t launch_split_for(const DecodeArgs& a, int bits, int hg, int B, hipStream_t stream, hipEvent_t ps,
+                            hipEvent_t pe) {
+  return bits == 2   ? launch_split_hg<2, ROPE>(a, hg, B, stream, ps, pe)
+         : bits == 3 ? launch_split_hg<3, ROPE>(a, hg, B, stream, ps, pe)
+                     : launch_split_hg<4, ROPE>(a, hg, B, stream, ps, pe);
 }
 
 hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, const AppendArgs& app, const void* q,
@@ -1188,10 +1203,9 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
   a.rope_in = L.rope ? reinterpret_cast<const float*>(base + L.ropein_off) : nullptr;
   const int hg = L.Hq / L.Hkv;
   hipError_t e;
-  if (prof_start && hipEventRecord(prof_start, stream) != hipSuccess) return hipGetLastError();
-  e = L.rope ? launch_split_for<true>(a, L.bits, hg, L.B, stream) : launch_split_for<false>(a, L.bits, hg, L.B, stream);
+  e = L.rope ? launch_split_for<true>(a, L.bits, hg, L.B, stream, prof_start, prof_stop)
+             : launch_split_for<false>(a, L.bits, hg, L.B, stream, prof_start, prof_stop);
   if (e != hipSuccess) return e;
-  if (prof_stop && hipEventRecord(prof_stop, stream) != hipSuccess) return hipGetLastError();
   return launch_combine(a.part, out, L.Hq, L.B, plan, L.win_blocks, stream);
 }
 

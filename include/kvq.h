@@ -152,10 +152,12 @@ kvq_status kvq_decode_step(kvq_cache* c, const void* k, const void* v, const int
  * reads (0 restores the automatic choice). Must be 0 or in [4, 1 << 20]. */
 kvq_status kvq_set_decode_split(kvq_cache* c, int32_t groups_per_split);
 
-/* Record `start` before and `stop` after the decode split kernel on the stream
- * passed to every later kvq_decode_attention call (both NULL to stop). Lets a
- * caller time that kernel alone with hipEventElapsedTime. The events are owned by
- * the caller; the library only records them. */
+/* Attach `start` and `stop` to the decode split kernel of every later decode call
+ * (kvq_decode_attention, kvq_decode_step) on that call's stream (both NULL to stop):
+ * the kernel is then launched with hipExtLaunchKernelGGL, which sets the events to
+ * its own start and end timestamps, so hipEventElapsedTime gives the kernel's
+ * duration as a kernel trace reports it. The events are owned by the caller; the
+ * library only passes them to the launch. */
 kvq_status kvq_set_profile_events(kvq_cache* c, hipEvent_t start, hipEvent_t stop);
 
 /* Destroy a handle (NULL is accepted). Synchronizes the creation stream first and
