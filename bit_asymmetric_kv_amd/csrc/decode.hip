@@ -1072,6 +1072,47 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   }
 }
 
+// Many (sequence, query head) rows with few partials each (large batches): one wave
+// merges one row over all 128 channels (two per lane, 8-byte loads), four rows per
+// workgroup, so the whole merge is one round of workgroups instead of one workgroup
+// per 16-channel slice of every row.
+constexpr int kRowWaves = 4;
+// Rows from which the one-wave-per-row merge is used.
+constexpr int kRowsCombineMin = 512;
+
+__global__ __launch_bounds__(64 * kRowWaves) void combine_rows_kernel(const float* __restrict__ part,
+                                                                      float* __restrict__ out, int Hq, int rows,
+                                                                      const SplitPlan plan, int wblocks) {
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int row = int(blockIdx.x) * kRowWaves + wave;  // b * Hq + hq
+  if (row >= rows) return;
+  const int nparts = splits_of(plan, row / Hq) + wblocks;
+  const float* p = part + size_t(row) * size_t(plan.pstride) * kPartialStride;
+  constexpr int kBatch = 8;
+  float m = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int i0 = 0; i0 < nparts; i0 += kBatch) {
+    float mi[kBatch], li[kBatch];
+    float2 oi[kBatch];
+    for (int u = 0; u < kBatch; u++) {
+      const int i = i0 + u;
+      const float* pi = p + size_t(i < nparts ? i : 0) * kPartialStride;
+      mi[u] = i < nparts ? pi[0] : -INFINITY;
+      li[u] = pi[1];
+      oi[u] = *reinterpret_cast<const float2*>(pi + 2 + 2 * lane);
+    }
+    for (int u = 0; u < kBatch; u++) {
+      const float mn = fmaxf(m, mi[u]);
+      const float a = m == -INFINITY ? 0.0f : exp2f(m - mn);
+      const float c = mi[u] == -INFINITY ? 0.0f : exp2f(mi[u] - mn);
+      l = l * a + li[u] * c;
+      o0 = o0 * a + oi[u].x * c;
+      o1 = o1 * a + oi[u].y * c;
+      m = mn;
+    }
+  }
+  *reinterpret_cast<float2*>(out + size_t(row) * kD + 2 * lane) = make_float2(o0 / l, o1 / l);
+}
+
 template <int BITS, int HG, bool ROPE>
 int resident_blocks_of() {
   int per_cu = 0;
@@ -1211,8 +1252,13 @@ hipError_t launch_decode(const Layout& L, uint8_t* base, const SeqDesc* seq, con
 
 hipError_t launch_combine(const float* part, float* out, int Hq, int B, const SplitPlan& plan, int wblocks,
                           hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(Hq, B, kD / kCombineChannels), dim3(kCombineThreads), 0, stream, part, out,
-                     Hq, plan, wblocks);
+  const int64_t rows = int64_t(B) * Hq;
+  if (rows >= kRowsCombineMin && rows <= INT32_MAX)
+    hipLaunchKernelGGL(combine_rows_kernel, dim3(unsigned((rows + kRowWaves - 1) / kRowWaves)), dim3(64 * kRowWaves),
+                       0, stream, part, out, Hq, int(rows), plan, wblocks);
+  else
+    hipLaunchKernelGGL(combine_kernel, dim3(Hq, B, kD / kCombineChannels), dim3(kCombineThreads), 0, stream, part,
+                       out, Hq, plan, wblocks);
   return hipGetLastError();
 }
 

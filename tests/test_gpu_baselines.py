@@ -75,3 +75,10 @@ def test_fp16_decode_head_ratios(dev, Hq, Hkv):
 def test_fp16_decode_long_many_splits(dev):
     # 40,000 tokens in one (b, h): many splits, chunks of a ragged tail, explicit scale
     _fp16_case(dev, 1, 4, 1, [40000], 40000, 13, scale=0.1)
+
+
+def test_fp16_decode_many_rows(dev):
+    # 64 sequences x 8 query heads = 512 (sequence, head) rows: the one-wave-per-row merge
+    rng = np.random.default_rng(14)
+    lens = rng.integers(1, 400, size=64).tolist()
+    _fp16_case(dev, 64, 8, 2, lens, 400, 14)
