@@ -752,15 +752,18 @@ kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const 
     max_groups = std::max(max_groups, Q[b] / kvq::kGroup);
     sum_groups += Q[b] / kvq::kGroup;
   }
-  // Equal lengths: one round of equal workgroups. Unequal lengths: about three
-  // rounds of smaller ones, longest sequences first.
+  // Equal lengths: one round of equal workgroups. Unequal lengths: about one and a
+  // half rounds of smaller ones, longest sequences first.
   const bool uniform_lengths = sum_groups == max_groups * B;
   int64_t gps = c->groups_per_split;
   if (gps == 0 && max_groups > 0) {
     // As many split workgroups as fit on the device at once next to the FP16-window
     // workgroups, each reading about the same number of groups, so a sequence gets
     // splits in proportion to its length. With unequal lengths the splits are made
-    // three times finer, so that the last splits of the sequences even out.
+    // 1.5 times finer, so that the short sequences' single splits fill the slots the
+    // long ones leave (64 sequences of 2K-32K tokens: 1.5 rounds measured 6 % faster
+    // than 2 or 3 rounds, whose workgroups each pay the start-up and merge again, and
+    // faster than 1.1 rounds, whose last workgroups run alone).
     if (c->resident_blocks == 0) {
       c->blocks_per_cu = kvq::decode_blocks_per_cu(c->cfg.bits, c->cfg.num_q_heads / c->cfg.num_kv_heads,
                                                    c->cfg.rope);
@@ -769,8 +772,9 @@ kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const 
     const int64_t win = int64_t(B) * Hkv * c->L.win_blocks;
     const int64_t slots = std::max<int64_t>(int64_t(B) * Hkv,
                                             c->resident_blocks - std::min<int64_t>(win, c->resident_blocks / 4));
-    const int64_t rounds = uniform_lengths ? 1 : 3;
-    gps = std::max<int64_t>(kvq::kMinGroupsPerSplit, (sum_groups * Hkv + slots * rounds - 1) / (slots * rounds));
+    const int64_t half_rounds = uniform_lengths ? 2 : 3;
+    gps = std::max<int64_t>(kvq::kMinGroupsPerSplit,
+                            (2 * sum_groups * Hkv + slots * half_rounds - 1) / (slots * half_rounds));
   }
   if (gps == 0) gps = kvq::kMinGroupsPerSplit;
   // Every sequence's split count must stay within the partial slots.
