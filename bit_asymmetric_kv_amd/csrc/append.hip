@@ -118,9 +118,11 @@ __global__ __launch_bounds__(64) void flush_wave_kernel(const GroupStore store, 
   constexpr int CB = kG * kD * BITS / 8;  // bytes of one code section
   // key and value codes [token][channel]; with rotation the same bytes first hold the
   // rotated keys [token][channel] on their way to the per-channel layout
+  // Key-code rows are padded by 4 bytes: the gather below reads one byte from each of
+  // 16 token rows at once, which with 128-byte rows all fall in one bank.
   __shared__ union {
     struct {
-      uint8_t ck[kG][kD];
+      uint8_t ck[kG][kD + 4];
       uint8_t cv[kG][kD];
     } c;
     __half kt[kG][kD];
@@ -131,16 +133,29 @@ __global__ __launch_bounds__(64) void flush_wave_kernel(const GroupStore store, 
   __shared__ __half vsz[2][kD];   // value scales / zero-points in block order
 
   const int lane = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const SeqDesc sd = seq.inl_valid ? seq.inl[b] : seq.dev[b];
-  const int nflush = (sd.q_new - sd.q_old) / kG;
+  // The record is the same for the whole wave: its fields go to scalar registers, so
+  // that the row addresses below are wave-uniform arithmetic.
+  const SeqDesc sdl = seq.inl_valid ? seq.inl[b] : seq.dev[b];
+  const int t_old = __builtin_amdgcn_readfirstlane(sdl.t_old);
+  const int q_old = __builtin_amdgcn_readfirstlane(sdl.q_old);
+  const int q_new = __builtin_amdgcn_readfirstlane(sdl.q_new);
+  const int nflush = (q_new - q_old) / kG;
   if (int(blockIdx.x) >= nflush) return;
-  const int g = sd.q_old / kG + blockIdx.x;
+  const int g = q_old / kG + blockIdx.x;
   const int t0 = sink + g * kG;  // with an attention sink, group g starts at token 1 + 32 g
   const size_t bh = size_t(b) * Hkv + h;
-  // Row of token t: FP16 window slot t % W if it was appended before, else input row.
-  auto row = [&](const __half* ring, const __half* in, int t) -> const __half* {
-    return t < sd.t_old ? ring + (bh * RS + size_t(t % W)) * kD
-                        : in + ((size_t(b) * n_max + (t - sd.t_old)) * Hkv + h) * kD;
+  // Row of token t0 + i (0 <= i < 32): FP16 window slot (t0 + i) % W if it was appended
+  // before, else input row. W = R + 32 >= 32, so the slots of the group's 32
+  // consecutive tokens wrap around the window at most once. The input offset of row 0
+  // is negative when the group starts inside the window; it is used only for rows
+  // t >= t_old, whose offsets are not.
+  const int s0 = t0 % W;
+  const int64_t ring_off0 = (int64_t(bh) * RS + s0) * kD;
+  const int64_t in_off0 = ((int64_t(b) * n_max + (t0 - t_old)) * Hkv + h) * kD;
+  const int64_t in_step = int64_t(Hkv) * kD;
+  auto row = [&](const __half* ring, const __half* in, int i) -> const __half* {
+    if (t0 + i >= t_old) return in + (in_off0 + int64_t(i) * in_step);
+    return ring + (ring_off0 + int64_t(s0 + i >= W ? i - W : i) * kD);
   };
   uint8_t* blk = store.at(b, h, g);
 
@@ -150,14 +165,14 @@ __global__ __launch_bounds__(64) void flush_wave_kernel(const GroupStore store, 
   uint32_t ku[kG];
   uint4 kr[8];
   if constexpr (ROT) {
-    const uint4* src = reinterpret_cast<const uint4*>(row(ringk, kin, t0 + lane / 2) + 64 * (lane % 2));
+    const uint4* src = reinterpret_cast<const uint4*>(row(ringk, kin, lane / 2) + 64 * (lane % 2));
     for (int q = 0; q < 8; q++) kr[q] = src[q];
   } else {
-    for (int i = 0; i < kG; i++) ku[i] = *reinterpret_cast<const uint32_t*>(row(ringk, kin, t0 + i) + 2 * lane);
+    for (int i = 0; i < kG; i++) ku[i] = *reinterpret_cast<const uint32_t*>(row(ringk, kin, i) + 2 * lane);
   }
   uint4 vu[2][4];
   for (int k = 0; k < 2; k++) {
-    const uint4* src = reinterpret_cast<const uint4*>(row(ringv, vin, t0 + 16 * k + lane / 4) + kG * (lane % 4));
+    const uint4* src = reinterpret_cast<const uint4*>(row(ringv, vin, 16 * k + lane / 4) + kG * (lane % 4));
     for (int q = 0; q < 4; q++) vu[k][q] = src[q];
   }
 
@@ -178,7 +193,7 @@ __global__ __launch_bounds__(64) void flush_wave_kernel(const GroupStore store, 
           y[8 * q + 2 * e + 1] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[e] >> 16)));
         }
       }
-      if (t0 + tl >= sd.t_old) {  // the partner lane (same token) takes the same branch
+      if (t0 + tl >= t_old) {  // the partner lane (same token) takes the same branch
         for (int hw = 1; hw < 64; hw <<= 1)
           for (int j = 0; j < 64; j += 2 * hw)
             for (int k = j; k < j + hw; k++) {
