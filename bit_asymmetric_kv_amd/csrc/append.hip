@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64) void flush_wave_kernel(const GroupStore store, 
   const int lane = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
   // The record is the same for the whole wave: its fields go to scalar registers, so
   // that the row addresses below are wave-uniform arithmetic.
-  const SeqDesc sdl = seq.inl_valid ? seq.inl[b] : seq.dev[b];
+  const SeqDesc sdl = seq_record(seq, seq.dev, b);
   const int t_old = __builtin_amdgcn_readfirstlane(sdl.t_old);
   const int q_old = __builtin_amdgcn_readfirstlane(sdl.q_old);
   const int q_new = __builtin_amdgcn_readfirstlane(sdl.q_new);
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(128) void ring_write_kernel(__half* __restrict__ ri
   __shared__ float row[kD];
   __shared__ int one;
   const int h = blockIdx.y, b = blockIdx.z;
-  const SeqDesc sd = seq.inl_valid ? seq.inl[b] : seq.dev[b];
+  const SeqDesc sd = seq_record(seq, seq.dev, b);
   if (seq.inl_valid && blockIdx.x == 0 && h == 0 && threadIdx.x == 0) seq.state[b] = sd;
   const int t_new = sd.t_old + sd.n_new;
   const int sink_new = (sink && sd.t_old == 0 && sd.n_new > 0) ? 1 : 0;

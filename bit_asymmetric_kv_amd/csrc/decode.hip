@@ -520,7 +520,7 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
   // Small batches pass every sequence's record in the arguments (the host mirror of
   // the lengths this launch sees), so no workgroup waits on a record load before
   // its first group loads go out.
-  const SeqDesc sd = a.app.seq.inl_valid ? a.app.seq.inl[b] : a.seq[b];
+  const SeqDesc sd = seq_record(a.app.seq, a.seq, b);
   const int T = sd.t_old + sd.n_new, Q = sd.q_new;
   const int ng = Q / kG;
 

@@ -41,6 +41,21 @@ struct SeqArgs {
   int inl_valid;
 };
 
+// The record of sequence b (wave-uniform). The inline copy is read on its own from
+// the kernel arguments, so that it comes through scalar loads; choosing between the
+// two sources by address made it a vector load from a generic address, which the
+// workgroup waited on before its first loads.
+__device__ inline SeqDesc seq_record(const SeqArgs& s, const SeqDesc* dev, int b) {
+  SeqDesc r = s.inl[s.inl_valid ? b : 0];
+  if (!s.inl_valid) {
+    // a load of another kind, so that it is not merged with the one above
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 d = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(dev) + b);
+    r = SeqDesc{d[0], d[1], d[2], d[3]};
+  }
+  return r;
+}
+
 // An append folded into a decode launch (caches without rotation): the FP16-window
 // workgroups read the appended tokens from k / v ([B][n_max][Hkv][128] fp16), write
 // the tokens that stay in the window to the ring, and with inline records store them
