@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256, HG == 8 ? 1 : 2) void fp16_split_kernel(Fp16Ar
     for (int hh = 0; hh < HG; hh++) {
       const float mh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hh));
       const float mn = fmaxf(m[hh], mh);
-      alpha[hh] = m[hh] == -INFINITY ? 0.0f : exp2f(m[hh] - mn);
+      alpha[hh] = m[hh] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[hh] - mn);
       grew = grew || mn != m[hh];
       m[hh] = mn;
     }
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256, HG == 8 ? 1 : 2) void fp16_split_kernel(Fp16Ar
     float ps = 0.0f;
     for (int i = 0; i < 8; i++) {
       const int tk = i < 4 ? 4 * kb + i : 16 + 4 * kb + (i - 4);
-      x[i] = exp2f(x[i] - mcol);
+      x[i] = __builtin_amdgcn_exp2f(x[i] - mcol);  // non-positive argument; -inf gives 0
       ps += x[i];
       if (col < HG) pst[wave][tk][col] = x[i];
     }
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256, HG == 8 ? 1 : 2) void fp16_split_kernel(Fp16Ar
       res = M;
     } else if (M != -INFINITY) {
       for (int w = 0; w < kWaves; w++)
-        if (wpart[w][hh][0] != -INFINITY) res += wpart[w][hh][c] * exp2f(wpart[w][hh][0] - M);
+        if (wpart[w][hh][0] != -INFINITY) res += wpart[w][hh][c] * __builtin_amdgcn_exp2f(wpart[w][hh][0] - M);
     }
     a.part[((size_t(b) * a.Hq + h * HG + hh) * a.nsplit + split) * kPartialStride + c] = res;
   }

@@ -277,24 +277,38 @@ struct WaveParts {
   __device__ float& at(int w, int hh, int c) const { return base[w * stride + hh * kPartialStride + c]; }
 };
 
-// Merge the per-wave partials and write the workgroup's partial.
+// exp2 of a non-positive argument (a softmax weight or rescale factor): the hardware
+// instruction; -inf gives 0, and results below the fp32 normal range, which it may
+// flush, are negligible next to the weight 1 of the maximum.
+__device__ inline float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Merge the per-wave partials and write the workgroup's partial. The factor
+// 2^(m_w - M) of wave w is formed once per query head; a wave without tokens (m_w =
+// -inf) has no o entries and is skipped.
 template <int HG>
 __device__ void merge_and_store(const DecodeArgs& a, int b, int h, int split, const WaveParts& wp) {
+  __shared__ float fac[HG][kWaves + 1];  // per head: the waves' factors, then M
   __syncthreads();
-  for (int idx = threadIdx.x; idx < HG * kPartialStride; idx += blockDim.x) {
-    int hh = idx / kPartialStride, c = idx % kPartialStride;
+  if (threadIdx.x < HG) {
+    const int hh = threadIdx.x;
     float M = -INFINITY;
     for (int w = 0; w < kWaves; w++) M = fmaxf(M, wp.at(w, hh, 0));
-    float r;
+    for (int w = 0; w < kWaves; w++) {
+      const float mw = wp.at(w, hh, 0);
+      fac[hh][w] = mw == -INFINITY ? 0.0f : exp2_nonpos(mw - M);
+    }
+    fac[hh][kWaves] = M;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < HG * kPartialStride; idx += blockDim.x) {
+    const int hh = idx / kPartialStride, c = idx % kPartialStride;
+    float r = 0.0f;
     if (c == 0) {
-      r = M;
-    } else if (M == -INFINITY) {
-      r = 0.0f;
+      r = fac[hh][kWaves];
     } else {
-      r = 0.0f;
       for (int w = 0; w < kWaves; w++) {
-        float mw = wp.at(w, hh, 0);
-        if (mw != -INFINITY) r += wp.at(w, hh, c) * exp2f(mw - M);
+        const float f = fac[hh][w];
+        if (wp.at(w, hh, 0) != -INFINITY) r = __builtin_fmaf(wp.at(w, hh, c), f, r);
       }
     }
     partial_ptr(a, b, h * HG + hh, split)[c] = r;
@@ -394,7 +408,7 @@ __device__ void window_chunk(const DecodeArgs& a, int b, int h, int t0, int cnt,
     const float sc = kval ? x * expo[hh] : -INFINITY;
     float m = sc;
     for (int off = 16; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    p[hh] = kval ? exp2f(sc - m) : 0.0f;
+    p[hh] = kval ? exp2_nonpos(sc - m) : 0.0f;
     float l = p[hh];
     for (int off = 16; off > 0; off >>= 1) l += __shfl_xor(l, off);
     if (lane == 0) {
@@ -697,6 +711,7 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
   float4v oacc[8];
   for (int t = 0; t < 8; t++) oacc[t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
+  bool started = false;  // wave-uniform: a group's softmax has run
   float zacc[NJ];
   for (int jr = 0; jr < NJ; jr++) zacc[jr] = 0.0f;
 
@@ -870,12 +885,15 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
     for (int i = 1; i < SP; i++) mloc = fmaxf(mloc, x[i]);
     if (__ballot(mloc > m_run)) {
       const float m_new = fmaxf(m_run, row_class_max<NR>(wave_max_rows(mloc)));
-      const float alpha = m_run == -INFINITY ? 0.0f : exp2f(ex * (m_run - m_new));
-      for (int t = 0; t < 8; t++) oacc[t] *= alpha;
-      l_run *= alpha;
-      for (int jr = 0; jr < NJ; jr++) zacc[jr] *= alpha;
+      if (started) {  // before the first group the sums are zero
+        const float alpha = exp2_nonpos(ex * (m_run - m_new));
+        for (int t = 0; t < 8; t++) oacc[t] *= alpha;
+        l_run *= alpha;
+        for (int jr = 0; jr < NJ; jr++) zacc[jr] *= alpha;
+      }
       m_run = m_new;
     }
+    started = true;
     const float negm = -ex * m_run;
     float p[8];
     if constexpr (NR == 1) {
@@ -1045,8 +1063,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
     }
     for (int u = 0; u < kBatch; u++) {
       const float mn = fmaxf(m, mi[u]);
-      const float a = m == -INFINITY ? 0.0f : exp2f(m - mn);
-      const float c = mi[u] == -INFINITY ? 0.0f : exp2f(mi[u] - mn);
+      const float a = m == -INFINITY ? 0.0f : exp2_nonpos(m - mn);
+      const float c = mi[u] == -INFINITY ? 0.0f : exp2_nonpos(mi[u] - mn);
       l = l * a + li[u] * c;
       o = o * a + oi[u] * c;
       m = mn;
@@ -1064,7 +1082,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
     float L = 0.0f, acc = 0.0f;
     for (int s2 = 0; s2 < kCombineSlices; s2++) {
       if (sm[s2] == -INFINITY) continue;
-      const float w = exp2f(sm[s2] - M);
+      const float w = exp2_nonpos(sm[s2] - M);
       L += sl[s2] * w;
       acc += so[s2][dl] * w;
     }
@@ -1102,8 +1120,8 @@ __global__ __launch_bounds__(64 * kRowWaves) void combine_rows_kernel(const floa
     }
     for (int u = 0; u < kBatch; u++) {
       const float mn = fmaxf(m, mi[u]);
-      const float a = m == -INFINITY ? 0.0f : exp2f(m - mn);
-      const float c = mi[u] == -INFINITY ? 0.0f : exp2f(mi[u] - mn);
+      const float a = m == -INFINITY ? 0.0f : exp2_nonpos(m - mn);
+      const float c = mi[u] == -INFINITY ? 0.0f : exp2_nonpos(mi[u] - mn);
       l = l * a + li[u] * c;
       o0 = o0 * a + oi[u].x * c;
       o1 = o1 * a + oi[u].y * c;
