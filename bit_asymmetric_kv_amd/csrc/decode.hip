@@ -38,6 +38,9 @@ namespace {
 constexpr int kD = kHeadDim;
 constexpr int kG = kGroup;
 constexpr int kWaves = 4;
+// Headroom of the split kernel's softmax reference above the running maximum, in
+// log2 units (a factor of 4).
+constexpr float kRefSlack = 2.0f;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -712,6 +715,12 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
   for (int t = 0; t < 8; t++) oacc[t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
   bool started = false;  // wave-uniform: a group's softmax has run
+  // Softmax reference with headroom: when a score passes the running reference, the
+  // reference moves kRefSlack log2 units above the new maximum, so the weights stay
+  // in (2^-kRefSlack, 1] of the maximum's and the sums are rescaled only when a score
+  // passes the reference again (in the prescaled units of this lane's head: ex is a
+  // power of two, so the quotient is exact).
+  const float ref_slack = kRefSlack / ex;
   float zacc[NJ];
   for (int jr = 0; jr < NJ; jr++) zacc[jr] = 0.0f;
 
@@ -879,12 +888,13 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
       x[i] = v + partner<U>(v);
     }
     // Online softmax. Scores stay in the prescaled units S (log2 units are ex * S);
-    // the running max m_run is kept in the same units.
-    // The cross-lane max is only formed when some score exceeds the running max.
+    // the running reference m_run (at least every score so far) is kept in the same
+    // units. The cross-lane max is only formed when some score exceeds it.
     float mloc = x[0];
     for (int i = 1; i < SP; i++) mloc = fmaxf(mloc, x[i]);
     if (__ballot(mloc > m_run)) {
-      const float m_new = fmaxf(m_run, row_class_max<NR>(wave_max_rows(mloc)));
+      const float hmax = row_class_max<NR>(wave_max_rows(mloc));
+      const float m_new = hmax > m_run ? hmax + ref_slack : m_run;
       if (started) {  // before the first group the sums are zero
         const float alpha = exp2_nonpos(ex * (m_run - m_new));
         for (int t = 0; t < 8; t++) oacc[t] *= alpha;
