@@ -716,10 +716,10 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
   float m_run = -INFINITY, l_run = 0.0f;
   bool started = false;  // wave-uniform: a group's softmax has run
   // Softmax reference with headroom: when a score passes the running reference, the
-  // reference moves kRefSlack log2 units above the new maximum, so the weights stay
-  // in (2^-kRefSlack, 1] of the maximum's and the sums are rescaled only when a score
-  // passes the reference again (in the prescaled units of this lane's head: ex is a
-  // power of two, so the quotient is exact).
+  // reference moves kRefSlack log2 units above the new maximum, so every weight stays
+  // at most 1, the maximum's at least 2^-kRefSlack, and the sums are rescaled only
+  // when a score passes the reference again (in the prescaled units of this lane's
+  // head: ex is a power of two, so the quotient is exact).
   const float ref_slack = kRefSlack / ex;
   float zacc[NJ];
   for (int jr = 0; jr < NJ; jr++) zacc[jr] = 0.0f;
