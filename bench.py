@@ -362,7 +362,70 @@ def summarize_traffic(dec_fetch, dec_write, copy_fetch, copy_write, workload, ou
     print(json.dumps({workload: res}))
 
 
+def _counters_per_dispatch(path, kernel_substr):
+    """Every counter of the kernels matching kernel_substr under a rocprofv3 --pmc
+    output folder, summed over its samples (shader engines, dies) per dispatch and
+    averaged over the dispatches."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if kernel_substr in r["Kernel_Name"]:
+                k = (r["Counter_Name"], r["Dispatch_Id"])
+                vals[k] = vals.get(k, 0.0) + float(r["Counter_Value"])
+    per = {}
+    for (c, _), v in vals.items():
+        per.setdefault(c, []).append(v)
+    if not per:
+        raise SystemExit(f"no counter samples for kernels matching {kernel_substr!r} under {path}")
+    return {c: sum(v) / len(v) for c, v in per.items()}
+
+
+def summarize_issue(sq1, sq2, workload, groups, waves_per_simd, out_path):
+    """Instruction-issue figures of the decode split kernel from two rocprofv3 --pmc
+    runs of SQ counters (the two passes of the counter summaries in profiles/):
+    instructions per 32-token group and wave, and the share of the SIMDs' cycles that
+    issue vector ALU work or any instruction (per-wave fractions of SQ_WAVE_CYCLES
+    times the waves that share a SIMD). Merged into out_path under
+    workloads[workload]."""
+    groups, waves_per_simd = int(groups), int(waves_per_simd)
+    c = _counters_per_dispatch(sq1, "decode_split_kernel")
+    c.update(_counters_per_dispatch(sq2, "decode_split_kernel"))
+    need = ("SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_ANY",
+            "SQ_WAIT_INST_ANY")
+    missing = [k for k in need if k not in c]
+    if missing:
+        raise SystemExit(f"counters missing from the runs: {missing}")
+    wc = c["SQ_WAVE_CYCLES"]
+    res = {"valu_instructions_per_group": round(c["SQ_INSTS_VALU"] / groups, 1),
+           "mfma_per_group": round(c["SQ_INSTS_MFMA"] / groups, 2),
+           "lds_per_group": round(c["SQ_INSTS_LDS"] / groups, 1) if "SQ_INSTS_LDS" in c else None,
+           "vmem_reads_per_group": round(c["SQ_INSTS_VMEM_RD"] / groups, 2) if "SQ_INSTS_VMEM_RD" in c else None,
+           "valu_active_per_wave_cycle": round(c["SQ_ACTIVE_INST_VALU"] / wc, 4),
+           "any_issue_per_wave_cycle": round(c["SQ_ACTIVE_INST_ANY"] / wc, 4),
+           "wait_per_wave_cycle": round(c["SQ_WAIT_INST_ANY"] / wc, 4),
+           "waves_per_simd": waves_per_simd,
+           "simd_valu_busy_frac": round(min(1.0, waves_per_simd * c["SQ_ACTIVE_INST_VALU"] / wc), 3),
+           "simd_issue_frac": round(min(1.0, waves_per_simd * c["SQ_ACTIVE_INST_ANY"] / wc), 3),
+           "groups_per_launch": groups,
+           "kernel_source_sha256": kernel_source_hash()}
+    data = {"workloads": {}}
+    if os.path.exists(out_path):
+        with open(out_path) as f:
+            old = json.load(f)
+        if "workloads" in old:
+            data = old
+    data["workloads"][workload] = res
+    with open(out_path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps({workload: res}))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-issue":
+        summarize_issue(*sys.argv[2:8])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--calibrate-copy":
         calibrate_copy()
         return
@@ -387,6 +450,8 @@ def main():
                     help="skip the streaming-read probe and the FP16-cache decode")
     ap.add_argument("--warm-iters", type=int, default=30,
                     help="extra decode calls on one cache to report a last-level-cache-resident time (0: skip)")
+    ap.add_argument("--issue-json", default=os.path.join(ROOT, "profiles", "issue.json"),
+                    help="instruction-issue figures from rocprofv3 SQ counters (--summarize-issue)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters, if present")
     args = ap.parse_args()
@@ -559,6 +624,18 @@ def main():
         except (OSError, ValueError):
             traffic = None
 
+    issue = None
+    if os.path.exists(args.issue_json):
+        try:
+            with open(args.issue_json) as f:
+                t = json.load(f).get("workloads", {}).get(w.name, {})
+            if t.get("kernel_source_sha256") == kernel_source_hash():
+                issue = {k: t[k] for k in ("simd_valu_busy_frac", "simd_issue_frac", "valu_instructions_per_group",
+                                           "mfma_per_group", "waves_per_simd")}
+                issue["source"] = "rocprofv3 SQ counters of this kernel source (profiles/issue.json)"
+        except (OSError, ValueError, KeyError):
+            issue = None
+
     comp = None
     if not args.no_comparisons:
         print("[bench] streaming-read probe and FP16-cache decode", file=sys.stderr, flush=True)
@@ -616,6 +693,7 @@ def main():
                                 f"{'true' if w.rope else 'false'}>"),
                      "limiter": "vector instruction issue and latency (rocprofv3 SQ counters), below the HBM "
                                 "ceiling",
+                     "issue": issue,
                      "frac_of_stream_read_2gib": (round(achieved / comp["hbm_stream_read_gbps"], 4)
                                                   if comp else None),
                      "frac_of_stream_read_same_bytes": (round(achieved / comp["stream_read_same_bytes_gbps"], 4)
