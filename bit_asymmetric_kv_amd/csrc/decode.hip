@@ -10,9 +10,9 @@
 // notes on KIVI's grouped/residual split).
 //
 // Work split (flash-decoding style): one workgroup per (sequence split of whole
-// groups, kv-head, sequence) plus one workgroup per (kv-head, sequence) for the FP16
-// window; each writes partial (max, sum, unnormalized output) per query head, and a
-// second kernel merges them.
+// groups, kv-head, sequence) plus, per (kv-head, sequence), the FP16 window's
+// workgroups (four 32-token chunks each, one per wave); each writes partial (max,
+// sum, unnormalized output) per query head, and a second kernel merges them.
 //
 // Inside a split each wave streams whole 32-token groups straight into registers,
 // issued three groups ahead of the group whose value side runs (two ahead of its
