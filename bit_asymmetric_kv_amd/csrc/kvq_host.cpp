@@ -779,6 +779,16 @@ kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const 
   if (gps == 0) gps = kvq::kMinGroupsPerSplit;
   // Every sequence's split count must stay within the partial slots.
   gps = std::max<int64_t>(gps, (max_groups + c->L.max_splits - 1) / c->L.max_splits);
+  // Equal sequences: keep the split count and spread the groups evenly over the
+  // splits. Rounding the count up left the last split of every sequence short (8
+  // sequences x 32 KV heads at 32K tokens: splits of 680 and 340 groups, so half the
+  // workgroups ended early and the long ones finished at one wave per SIMD; even
+  // splits of 510 made that step 11 % shorter).
+  if (c->groups_per_split == 0 && uniform_lengths && max_groups > 0) {
+    const int64_t n = (max_groups + gps - 1) / gps;
+    gps = std::max<int64_t>(kvq::kMinGroupsPerSplit, (max_groups + n - 1) / n);
+    gps = std::max<int64_t>(gps, (max_groups + c->L.max_splits - 1) / c->L.max_splits);
+  }
   kvq::SplitPlan plan{};
   int64_t max_split = 0;
   if (B <= kvq::kInlineSeqs) {
