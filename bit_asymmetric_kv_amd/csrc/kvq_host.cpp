@@ -812,16 +812,18 @@ kvq_status launch_decode_for(kvq_cache* c, const std::vector<int64_t>& T, const 
     plan.uniform = int32_t(max_split);
   }
   plan.pstride = int32_t(max_split) + c->L.win_blocks;
-  // One round of equal sequences at two workgroups per compute unit: the dispatcher
-  // fills every compute unit's first slot before its second, and a compute unit then
-  // issues from its older workgroup first, so the younger one trails and ends alone.
-  // Giving the first-dispatched half of the splits 1.7 times the groups of the second
-  // half lets both end together (measured against equal splits: about 7 % shorter
-  // steps at 128K tokens; 1.4, 1.5, 2, 2.5 and 3 measured slower than 1.7). Explicit
-  // split sizes keep equal splits.
+  // One round of equal sequences' splits at two workgroups per compute unit: the
+  // dispatcher fills every compute unit's first slot before its second, and a compute
+  // unit then issues from its older workgroup first, so the younger one trails and
+  // ends alone. Giving the first-dispatched half of the splits 1.7 times the groups of
+  // the second half lets both end together (measured against equal splits: about 7 %
+  // shorter steps at 128K tokens; 1.4, 1.5, 2, 2.5 and 3 measured slower than 1.7).
+  // FP16-window workgroups that do not fit in the same round follow the splits and do
+  // not change their placement (8 sequences x 32 KV heads at 32K tokens: 6 % shorter
+  // steps than equal splits). Explicit split sizes keep equal splits.
   plan.older_weight = 0.0f;
   if (c->groups_per_split == 0 && uniform_lengths && c->blocks_per_cu == 2 && max_split >= 2 &&
-      max_split * int64_t(B) * Hkv + int64_t(B) * Hkv * c->L.win_blocks <= c->resident_blocks)
+      max_split * int64_t(B) * Hkv <= c->resident_blocks)
     plan.older_weight = 1.7f;
   const float scale_log2 = c->cfg.softmax_scale * 1.4426950408889634f;
   const SeqDesc* dev_seq = reinterpret_cast<const SeqDesc*>(c->base + c->L.seq_off);
