@@ -386,9 +386,10 @@ def summarize_issue(sq1, sq2, workload, groups, waves_per_simd, out_path):
     """Instruction-issue figures of the decode split kernel from two rocprofv3 --pmc
     runs of SQ counters (the two passes of the counter summaries in profiles/):
     instructions per 32-token group and wave, and the share of the SIMDs' cycles that
-    issue vector ALU work or any instruction (per-wave fractions of SQ_WAVE_CYCLES
-    times the waves that share a SIMD). Merged into out_path under
-    workloads[workload]."""
+    issue vector ALU work (per-wave fraction of SQ_WAVE_CYCLES times the waves that
+    share a SIMD; one vector ALU per SIMD, so at most 1), and the same sum for
+    instructions of any kind in progress (units overlap, so it can pass 1). Merged
+    into out_path under workloads[workload]."""
     groups, waves_per_simd = int(groups), int(waves_per_simd)
     c = _counters_per_dispatch(sq1, "decode_split_kernel")
     c.update(_counters_per_dispatch(sq2, "decode_split_kernel"))
@@ -406,8 +407,8 @@ def summarize_issue(sq1, sq2, workload, groups, waves_per_simd, out_path):
            "any_issue_per_wave_cycle": round(c["SQ_ACTIVE_INST_ANY"] / wc, 4),
            "wait_per_wave_cycle": round(c["SQ_WAIT_INST_ANY"] / wc, 4),
            "waves_per_simd": waves_per_simd,
-           "simd_valu_busy_frac": round(min(1.0, waves_per_simd * c["SQ_ACTIVE_INST_VALU"] / wc), 3),
-           "simd_issue_frac": round(min(1.0, waves_per_simd * c["SQ_ACTIVE_INST_ANY"] / wc), 3),
+           "simd_valu_busy_frac": round(waves_per_simd * c["SQ_ACTIVE_INST_VALU"] / wc, 3),
+           "simd_any_active_per_cycle": round(waves_per_simd * c["SQ_ACTIVE_INST_ANY"] / wc, 3),
            "groups_per_launch": groups,
            "kernel_source_sha256": kernel_source_hash()}
     data = {"workloads": {}}
@@ -630,7 +631,7 @@ def main():
             with open(args.issue_json) as f:
                 t = json.load(f).get("workloads", {}).get(w.name, {})
             if t.get("kernel_source_sha256") == kernel_source_hash():
-                issue = {k: t[k] for k in ("simd_valu_busy_frac", "simd_issue_frac", "valu_instructions_per_group",
+                issue = {k: t[k] for k in ("simd_valu_busy_frac", "simd_any_active_per_cycle", "valu_instructions_per_group",
                                            "mfma_per_group", "waves_per_simd")}
                 issue["source"] = "rocprofv3 SQ counters of this kernel source (profiles/issue.json)"
         except (OSError, ValueError, KeyError):

@@ -102,7 +102,7 @@ def test_summarize_issue_fractions(tmp_path, monkeypatch):
     assert r["lds_per_group"] == 21.0 and r["vmem_reads_per_group"] == 6.5
     assert r["valu_active_per_wave_cycle"] == pytest.approx(0.28)
     assert r["simd_valu_busy_frac"] == pytest.approx(0.56)
-    assert r["simd_issue_frac"] == pytest.approx(0.8)
+    assert r["simd_any_active_per_cycle"] == pytest.approx(0.8)
     assert r["wait_per_wave_cycle"] == pytest.approx(0.25)
     assert r["kernel_source_sha256"] == "h"
 
