@@ -295,13 +295,21 @@ def measure_comparisons(torch, kvq, w, ev, stream, dev, nbytes, iters=20):
 
 
 COPY_BYTES = 1 << 30
-KERNEL_SOURCE = os.path.join(ROOT, "bit_asymmetric_kv_amd", "csrc", "decode.hip")
+# The decode kernel's sources: its own file and the header whose device helpers (the
+# group store, the sequence records) it compiles in.
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_asymmetric_kv_amd", "csrc", "decode.hip"),
+                  os.path.join(ROOT, "bit_asymmetric_kv_amd", "csrc", "kvq_internal.h")]
 
 
 def kernel_source_hash():
+    """sha256 over the decode kernel's sources, in order (counter summaries carry it,
+    so that they are used only for the device code they were measured on)."""
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def calibrate_copy():

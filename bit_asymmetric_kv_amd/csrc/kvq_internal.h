@@ -103,10 +103,15 @@ struct GroupStore {
     if (!table) return ((size_t(b) * Hkv + h) * size_t(gcap) + size_t(g)) * size_t(gb);
     return ((size_t(page) * Hkv + h) * size_t(P) + size_t(g & (P - 1))) * size_t(gb);
   }
-  // Device side: looks the page up in the table.
+  // Device side: looks the page up in the table. The table does not change while a
+  // kernel runs, so it is read through the constant address space: a wave-uniform
+  // index then gives one scalar load, whatever else the kernel does with memory
+  // (read as a generic global load, the entry came through a vector load that waited
+  // behind the group loads in flight).
   __device__ uint8_t* at(int b, int h, long long g) const {
+    typedef __attribute__((address_space(4))) const int32_t* const_i32p;
     const int page =
-        table ? __builtin_amdgcn_readfirstlane(table[size_t(b) * max_pages + size_t(g >> pshift)]) : 0;
+        table ? __builtin_amdgcn_readfirstlane(((const_i32p)table)[size_t(b) * max_pages + size_t(g >> pshift)]) : 0;
     return blocks + offset(b, h, g, page);
   }
 };
