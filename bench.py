@@ -370,6 +370,35 @@ def summarize_traffic(dec_fetch, dec_write, copy_fetch, copy_write, workload, ou
     print(json.dumps({workload: res}))
 
 
+def summarize_trace(trace_dir, workload, out_path):
+    """Average duration of the decode split kernel in a rocprofv3 --kernel-trace --stats
+    run (its kernel_stats.csv), stored in out_path under workloads[workload]["trace"]
+    with the kernel source hash, so that the bench line can give the kernel's own
+    time beside the event timing."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    calls = total_ns = 0
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if "decode_split_kernel" in r["Name"]:
+                calls += int(r["Calls"])
+                total_ns += float(r["TotalDurationNs"])
+    if not calls:
+        raise SystemExit(f"no decode_split_kernel rows in the kernel stats under {trace_dir}")
+    data = {"calibration": None, "workloads": {}}
+    if os.path.exists(out_path):
+        with open(out_path) as f:
+            old = json.load(f)
+        if "workloads" in old:
+            data = old
+    res = {"avg_us": round(total_ns / calls / 1e3, 3), "dispatches": calls, "kernel_source_sha256": kernel_source_hash()}
+    data["workloads"].setdefault(workload, {})["trace"] = res
+    with open(out_path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps({workload: res}))
+
+
 def _counters_per_dispatch(path, kernel_substr):
     """Every counter of the kernels matching kernel_substr under a rocprofv3 --pmc
     output folder, summed over its samples (shader engines, dies) per dispatch and
@@ -440,6 +469,9 @@ def main():
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-traffic":
         summarize_traffic(*sys.argv[2:8])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        summarize_trace(*sys.argv[2:5])
         return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -621,7 +653,7 @@ def main():
     for e in (ks, ke, wst, wen, [t_start, t_end]):
         ev.destroy(e)
 
-    traffic = None
+    traffic = traced_us = None
     if os.path.exists(args.traffic_json):
         try:
             with open(args.traffic_json) as f:
@@ -630,8 +662,11 @@ def main():
             t = t.get("workloads", {}).get(w.name, {})
             if t.get("kernel_source_sha256") == kernel_source_hash():
                 traffic = t.get("bytes_per_launch")
+            tr = t.get("trace") or {}
+            if tr.get("kernel_source_sha256") == kernel_source_hash():
+                traced_us = tr.get("avg_us")
         except (OSError, ValueError):
-            traffic = None
+            traffic = traced_us = None
 
     issue = None
     if os.path.exists(args.issue_json):
@@ -703,6 +738,12 @@ def main():
                      "limiter": "vector instruction issue and latency (rocprofv3 SQ counters), below the HBM "
                                 "ceiling",
                      "issue": issue,
+                     # the kernel's own average duration in a rocprofv3 kernel trace of this
+                     # workload and kernel source (profiles/traffic.json), and the fraction that
+                     # this run's algorithmic bytes per launch give over it
+                     "traced_kernel_us": traced_us,
+                     "frac_traced": (round(kbytes_avg / (traced_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+                                     if traced_us else None),
                      "frac_of_stream_read_2gib": (round(achieved / comp["hbm_stream_read_gbps"], 4)
                                                   if comp else None),
                      "frac_of_stream_read_same_bytes": (round(achieved / comp["stream_read_same_bytes_gbps"], 4)

@@ -117,6 +117,26 @@ def test_summarize_issue_needs_its_counters(tmp_path, monkeypatch):
                               str(tmp_path / "issue.json"))
 
 
+def test_summarize_trace_averages_the_split_kernel(tmp_path, monkeypatch):
+    """The traced average is total duration over calls of the split kernel rows only,
+    stored beside the workload's counter figures without disturbing them."""
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h")
+    d = tmp_path / "tr" / "host" / "123"
+    os.makedirs(d)
+    with open(d / "t_kernel_stats.csv", "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        wr.writerow(["void kvq::decode_split_kernel<2, 4, false>(DecodeArgs)", 200, 5_400_000, 27000, 50, 1, 1, 1])
+        wr.writerow(["void kvq::combine_kernel(float const*)", 200, 840_000, 4200, 10, 1, 1, 1])
+    out = tmp_path / "traffic.json"
+    json.dump({"calibration": None, "workloads": {"wk": {"bytes_per_launch": 5, "kernel_source_sha256": "h"}}},
+              open(out, "w"))
+    bench.summarize_trace(str(tmp_path / "tr"), "wk", str(out))
+    r = json.load(open(out))["workloads"]["wk"]
+    assert r["bytes_per_launch"] == 5
+    assert r["trace"] == {"avg_us": 27.0, "dispatches": 200, "kernel_source_sha256": "h"}
+
+
 def test_committed_counter_summaries_describe_the_committed_kernel():
     """profiles/traffic.json and profiles/issue.json: the bench only reports figures
     whose kernel source hash is the current one, so the committed files carry it."""
@@ -127,3 +147,5 @@ def test_committed_counter_summaries_describe_the_committed_kernel():
         for wname, r in d["workloads"].items():
             assert wname in wl.WORKLOADS, (name, wname)
             assert r["kernel_source_sha256"] == h, (name, wname)
+            if name == "traffic.json":
+                assert r["trace"]["kernel_source_sha256"] == h, wname
