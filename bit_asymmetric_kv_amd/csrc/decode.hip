@@ -1086,7 +1086,9 @@ __global__ __launch_bounds__(256, ((BITS == 4 && ROPE) || HG == 8) ? 2 : 1) void
 // are merged in shared memory.
 // The same for the combine: the lines holding the partial and output pointers, row
 // b's split count and the plan's scalars, read together. The plan follows the
-// pointers and Hq in the parameter list.
+// pointers and Hq in the parameter list. Split counts exist for the first
+// kInlineSeqs sequences only (larger batches use the plan's uniform count), so the
+// read stays inside the arguments for any b.
 constexpr unsigned kCombinePlanOffset = 2 * sizeof(void*) + sizeof(int);
 __device__ inline void warm_combine_lines(int b) {
   typedef __attribute__((address_space(4))) const char* karg_t;
@@ -1098,7 +1100,7 @@ __device__ inline void warm_combine_lines(int b) {
       "s_load_dword %2, %3, %5\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=s"(t0), "=s"(t1), "=s"(t2)
-      : "s"(kp), "s"(kp + kCombinePlanOffset + offsetof(SplitPlan, count) + 4 * b),
+      : "s"(kp), "s"(kp + kCombinePlanOffset + offsetof(SplitPlan, count) + 4 * min(b, kInlineSeqs - 1)),
         "i"(kCombinePlanOffset + offsetof(SplitPlan, use_prefix)));
 }
 

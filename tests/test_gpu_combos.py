@@ -78,3 +78,20 @@ def test_large_batch_paged_sink_rope(dev):
     for s in range(12):
         _step(p, np.ones(70, dtype=np.int64))
     p.check_state()
+
+
+def test_large_batch_sliced_combine(dev):
+    # 70 sequences with 2 query heads: 140 (sequence, query head) rows, below the
+    # row-merge threshold, so the sliced combine runs with sequence indices past the
+    # inline records (the plan's uniform split count)
+    w = wl.WORKLOADS["ragged_b64_wht"].scaled(batch=70, num_q_heads=2, num_kv_heads=2, rotate=False, residual=32,
+                                              name="combo_b70_sliced")
+    print("case combo B=70 Hq=2 sliced combine", flush=True)
+    p = _pair(w, 600, dev, False, seed=11)
+    ctx = np.random.default_rng(13).integers(1, 500, size=70)
+    p.append(ctx)
+    p.check_state()
+    p.check_decode()
+    for s in range(6):
+        _step(p, np.ones(70, dtype=np.int64))
+    p.check_decode()
