@@ -46,22 +46,32 @@ def _check_blocks(cache, oh, b, h, group_sample):
         assert np.array_equal(rv[slot].view(np.uint16), oh.v16[t].view(np.uint16)), f"ring value t={t}"
 
 
-def _run_full(w, dev, sample, steps, check_steps, group_sample=lambda ng: range(ng), one_call=False):
+def _run_full(w, dev, sample, steps, check_steps, group_sample=lambda ng: range(ng), one_call=False, page_groups=0):
     """one_call: each step is one kvq_decode_step (append + decode in one call, the
-    window write folded into the decode launch), as the bench times it."""
+    window write folded into the decode launch), as the bench times it. page_groups:
+    a paged cache, every sequence's pages in a seeded random order (as bench.py
+    --page-groups lays them out)."""
     import bit_asymmetric_kv_amd as kvq
     lens = w.context_lengths()
     max_tokens = int(lens.max()) + steps + 1
+    paged = {}
+    if page_groups:
+        max_pages = -(-((max_tokens + w.group - 1) // w.group) // page_groups)
+        paged = dict(page_groups=page_groups, pool_pages=w.batch * max_pages)
     cache = kvq.KVCache(w.batch, w.num_q_heads, w.num_kv_heads, bits=w.bits, group=w.group,
                         residual=w.residual, rotate=w.rotate, max_tokens=max_tokens, device=dev,
-                        sink=w.sink, rope=w.rope)
+                        sink=w.sink, rope=w.rope, **paged)
+    if page_groups:
+        perm = np.random.default_rng(w.seed + 5).permutation(w.batch * max_pages)
+        for b in range(w.batch):
+            cache.set_pages(b, perm[b * max_pages:(b + 1) * max_pages].tolist())
     oracles = {bh: OracleHead(w.bits, w.residual, w.rotate, sink=w.sink, rope=w.rope) for bh in sample}
     params = wl.torch_key_params(torch, w, dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed * 101 + 7)
     print(f"case full-size {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} bits={w.bits} "
           f"R={w.residual} rot={w.rotate} context max {int(lens.max())} steps={steps} sample={sample} "
-          f"one_call={one_call}", flush=True)
+          f"one_call={one_call} page_groups={page_groups}", flush=True)
     done = np.zeros(w.batch, dtype=np.int64)
     while np.any(done < lens):
         n = np.minimum(lens - done, CHUNK)
@@ -119,6 +129,13 @@ def test_full_gqa_128k_one_call_steps(dev):
     # the bench's step: kvq_decode_step with the automatic (weighted) split plan over
     # 40 steps, so one group leaves the window (T - R crosses 131072 + 32 at step 31)
     _run_full(wl.WORKLOADS["gqa_128k_2bit"], dev, [(0, 0), (0, 3), (0, 6)], 40, {0, 30, 31, 39}, one_call=True)
+
+
+def test_full_gqa_128k_paged_one_call_steps(dev):
+    # the paged headline as the bench times it: 16-group pages in random order, one-call
+    # steps across a group flush
+    _run_full(wl.WORKLOADS["gqa_128k_2bit"], dev, [(0, 1), (0, 7)], 36, {0, 34, 35}, one_call=True,
+              page_groups=16)
 
 
 def test_full_llama2_7b_b8_32k_one_call_steps(dev):
